@@ -1,0 +1,574 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU statement of what paged decode attention computes.
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  It shares no code, header, table or constant generator
+ * with the HIP library in paged_kv_cache_189_amd/csrc; everything here is
+ * written out from the definitions below.
+ *
+ * Sources (the pages), cited by title and section:
+ *  [P1] "Optimizing Llama 3.1 405B Inference with vLLM PagedAttention",
+ *       sections "Why Standard Attention Fails at Scale", "PagedAttention
+ *       Mechanics", "Quantization Without Quality Loss".
+ *  [P2] "Optimizing vLLM Throughput with PagedAttention and Continuous
+ *       Batching for Llama 3", "Key Tuning Insights" and the GQA paragraph.
+ *  [P3] "vLLM PagedAttention Optimization: Complete Step-by-Step Tuning Guide
+ *       for Low-Latency Inference", "How PagedAttention Solves the KV Cache
+ *       Bottleneck", "Step 1: Calculate KV Cache Memory Requirements",
+ *       "Step 3: Enable FP8 KV Cache for 2x Concurrency Expansion".
+ *  [P4] "vLLM PagedAttention: Memory Optimization & High-Throughput LLM
+ *       Inference Tuning", "1. The Anatomy of the KV Cache Bottleneck",
+ *       "2. PagedAttention: OS Virtual Memory for LLMs", "4. Continuous
+ *       Batching and Iteration-Level Scheduling".
+ *
+ * Readings where the pages are silent (the pages never write the attention
+ * formula, the softmax, the GQA map, the layout or the fp8 rounding):
+ *  - attention of one new query over all cached tokens of its sequence
+ *    ([P4] §1: the next token attends to every earlier token whose K and V
+ *    are cached), softmax(scale * q.k) weighted sum of v, evaluated in fp64
+ *    with the maximum subtracted before exp;
+ *  - GQA: query head h reads KV head h / (Hq / Hkv) (contiguous groups; [P2]
+ *    names GQA only);
+ *  - fp8 is OCP E4M3FN (bias 7, no infinities, S.1111.111 is NaN, max 448)
+ *    ([P1] "Quantization Without Quality Loss", [P3] Step 3 name E4M3);
+ *    a value is stored as satfinite round-to-nearest-even of fp32(x / scale);
+ *  - the pool layout is the library's (K tile [D/X][16][X] with X = 16 bytes
+ *    of elements, V tile [D][16], one tile per (block, kv head)); the oracle
+ *    reaches it only through k_index()/v_index() below.
+ *
+ * Parity pins for every function here live in tests/ (oracle self-checks);
+ * none of them is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_E4M3 = 2 };
+enum {
+  OR_OK = 0,
+  OR_INVALID = -1,
+  OR_OUT_OF_BLOCKS = -2,
+  OR_UNKNOWN_SEQ = -3,
+  OR_SEQ_EXISTS = -4,
+  OR_SHARED_TAIL = -5
+};
+
+/* ------------------------------------------------------------------------ */
+/* Value codecs                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* OCP E4M3FN, closed form: sign s, exponent field e (bias 7), mantissa m.
+ * e == 0 is subnormal: 2^-6 * m/8.  Code S.1111.111 is NaN. */
+double oracle_e4m3_decode(uint8_t code) {
+  int s = (code >> 7) & 1;
+  int e = (code >> 3) & 0xF;
+  int m = code & 0x7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, -6);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+/* Satfinite round-to-nearest-even into E4M3FN, by definition: the finite code
+ * nearest to x; on a tie the code with an even mantissa (even code); any
+ * magnitude beyond the largest finite value 448 gives +-448; NaN gives NaN.
+ * The search over every finite magnitude code is the definition itself. */
+uint8_t oracle_e4m3_encode(float x) {
+  double a;
+  int best = 0, c;
+  double best_d;
+  uint32_t bits;
+  memcpy(&bits, &x, 4);
+  uint8_t sign = (uint8_t)((bits >> 31) << 7);
+  if (isnan(x)) return (uint8_t)(sign | 0x7F);
+  a = fabs((double)x);
+  if (a > 448.0) return (uint8_t)(sign | 0x7E);
+  best_d = INFINITY;
+  for (c = 0; c <= 0x7E; ++c) {
+    double d = fabs(oracle_e4m3_decode((uint8_t)c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best_d = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(sign | best);
+}
+
+/* bf16 is the top half of an fp32 bit pattern. */
+double oracle_bf16_decode(uint16_t h) {
+  uint32_t bits = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &bits, 4);
+  return (double)f;
+}
+
+/* Round-to-nearest-even fp32 -> bf16: of the two bf16 values that bracket x
+ * (truncation toward zero, and one bf16 ulp further from zero), the nearer;
+ * on a tie the one whose last kept bit is 0.  The value one ulp above the
+ * largest finite bf16 is 2^128, which encodes as infinity. */
+uint16_t oracle_bf16_encode(float x) {
+  uint32_t bits;
+  memcpy(&bits, &x, 4);
+  if (isnan(x)) return (uint16_t)(((bits >> 16) & 0x8000) | 0x7FC0);
+  if (isinf(x)) return (uint16_t)(bits >> 16);
+  uint32_t lo = bits & 0xFFFF0000u;
+  uint32_t hi = lo + 0x10000u; /* next magnitude up (may become inf) */
+  double vx = fabs((double)x);
+  float flo;
+  memcpy(&flo, &lo, 4);
+  double vlo = fabs((double)flo);
+  double vhi;
+  if (((hi >> 23) & 0xFF) == 0xFF) {
+    vhi = ldexp(1.0, 128);
+  } else {
+    float fhi;
+    memcpy(&fhi, &hi, 4);
+    vhi = fabs((double)fhi);
+  }
+  double dlo = vx - vlo, dhi = vhi - vx;
+  if (dlo < dhi) return (uint16_t)(lo >> 16);
+  if (dhi < dlo) return (uint16_t)(hi >> 16);
+  return (((lo >> 16) & 1) == 0) ? (uint16_t)(lo >> 16) : (uint16_t)(hi >> 16);
+}
+
+void oracle_bf16_encode_array(const float* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_encode(x[i]);
+}
+void oracle_e4m3_encode_array(const float* x, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(x[i]);
+}
+
+static int elem_bytes(int dtype) {
+  return dtype == OR_F32 ? 4 : dtype == OR_BF16 ? 2 : dtype == OR_E4M3 ? 1 : 0;
+}
+
+/* Exact widening of a stored element to fp64. */
+static double widen(int dtype, const void* base, int64_t idx) {
+  if (dtype == OR_F32) return (double)((const float*)base)[idx];
+  if (dtype == OR_BF16) return oracle_bf16_decode(((const uint16_t*)base)[idx]);
+  return oracle_e4m3_decode(((const uint8_t*)base)[idx]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* KV byte accounting ([P3] Step 1): bytes per token over all layers =      */
+/* 2 (K and V) * layers * kv heads * head dim * bytes per element.          */
+/* ------------------------------------------------------------------------ */
+int64_t oracle_kv_bytes_per_token(int64_t layers, int64_t kv_heads, int64_t head_dim,
+                                  int64_t bytes_per_elem) {
+  return 2 * layers * kv_heads * head_dim * bytes_per_elem;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Pool layout: element (block b, kv head h, slot o, dim d).                 */
+/* K tile per (b, h): [D/X][BS][X], X = 16 / element bytes.                   */
+/* V tile per (b, h): [D][BS].                                                */
+/* ------------------------------------------------------------------------ */
+static int64_t k_index(int64_t b, int64_t h, int64_t o, int64_t d, int64_t H, int64_t D,
+                       int64_t BS, int64_t X) {
+  return (((b * H + h) * (D / X) + d / X) * BS + o) * X + d % X;
+}
+static int64_t v_index(int64_t b, int64_t h, int64_t o, int64_t d, int64_t H, int64_t D,
+                       int64_t BS) {
+  return ((b * H + h) * D + d) * BS + o;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Cache write ("appends to the logical sequence", [P1] PagedAttention        */
+/* Mechanics): each new token's K and V land in the slot the block table     */
+/* gave it.  slot = physical block * BS + offset; a slot of -1 is skipped.   */
+/* f32->f32 and bf16->bf16 copy bits; f32->bf16 rounds to nearest even;       */
+/* ->e4m3 stores satfinite RNE of the fp32 quotient x / scale.               */
+/* ------------------------------------------------------------------------ */
+static void store_elem(int cache_dtype, void* cache, int64_t idx, int src_dtype,
+                       const void* src, int64_t sidx, float scale) {
+  if (cache_dtype == OR_F32) {
+    ((float*)cache)[idx] = ((const float*)src)[sidx];
+  } else if (cache_dtype == OR_BF16) {
+    if (src_dtype == OR_BF16)
+      ((uint16_t*)cache)[idx] = ((const uint16_t*)src)[sidx];
+    else
+      ((uint16_t*)cache)[idx] = oracle_bf16_encode(((const float*)src)[sidx]);
+  } else {
+    float x = (float)widen(src_dtype, src, sidx); /* exact: src is f32 or bf16 */
+    float q = x / scale;                          /* IEEE fp32 division */
+    ((uint8_t*)cache)[idx] = oracle_e4m3_encode(q);
+  }
+}
+
+int oracle_reshape_and_cache(int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                             int64_t num_blocks, int src_dtype, const void* k_new,
+                             const void* v_new, int cache_dtype, void* k_cache, void* v_cache,
+                             const int64_t* slot_mapping, float k_scale, float v_scale) {
+  int64_t X = 16 / elem_bytes(cache_dtype);
+  for (int t = 0; t < num_tokens; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    if (slot >= num_blocks * block_size) return OR_INVALID;
+    int64_t b = slot / block_size, o = slot % block_size;
+    for (int h = 0; h < num_kv_heads; ++h)
+      for (int d = 0; d < head_dim; ++d) {
+        int64_t sidx = ((int64_t)t * num_kv_heads + h) * head_dim + d;
+        store_elem(cache_dtype, k_cache, k_index(b, h, o, d, num_kv_heads, head_dim, block_size, X),
+                   src_dtype, k_new, sidx, k_scale);
+        store_elem(cache_dtype, v_cache, v_index(b, h, o, d, num_kv_heads, head_dim, block_size),
+                   src_dtype, v_new, sidx, v_scale);
+      }
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention over the paged cache.                                    */
+/*                                                                            */
+/* For sequence s and query head h, with G = Hq / Hkv and g = h / G:         */
+/*   token t (0 <= t < L_s) lives in block table[s][t / BS] at offset t % BS */
+/*   ([P4] §2: logical blocks map to physical blocks through a block table;  */
+/*   the kernel walks that table);                                          */
+/*   sc_t = scale * sum_d q[s][h][d] * k_scale * K(t)[d]                      */
+/*   w_t  = exp(sc_t - max_u sc_u) / sum_u exp(sc_u - max_u sc_u)             */
+/*   out  = sum_t w_t * v_scale * V(t)[:]      lse = max + ln(sum exp(...))   */
+/* Everything in fp64 from the exactly widened stored values.  L_s == 0 gives */
+/* a zero row and lse = -inf.                                                 */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int S, Hq, Hkv, D, BS, max_blocks;
+  int q_dtype, cache_dtype;
+  const void *q, *k, *v;
+  const int32_t *tables, *lens;
+  double scale, k_scale, v_scale;
+} problem;
+
+/* scores of (s, h) for t in [t0, t1) into sc[t - t0] */
+static void scores(const problem* p, int s, int h, int t0, int t1, double* sc) {
+  int G = p->Hq / p->Hkv, g = h / G;
+  int64_t X = 16 / elem_bytes(p->cache_dtype);
+  for (int t = t0; t < t1; ++t) {
+    int64_t b = p->tables[(int64_t)s * p->max_blocks + t / p->BS];
+    int64_t o = t % p->BS;
+    double acc = 0.0;
+    for (int d = 0; d < p->D; ++d) {
+      double qd = widen(p->q_dtype, p->q, ((int64_t)s * p->Hq + h) * p->D + d);
+      double kd = widen(p->cache_dtype, p->k, k_index(b, g, o, d, p->Hkv, p->D, p->BS, X)) * p->k_scale;
+      acc += qd * kd;
+    }
+    sc[t - t0] = p->scale * acc;
+  }
+}
+
+static double v_at(const problem* p, int s, int g, int t, int d) {
+  int64_t b = p->tables[(int64_t)s * p->max_blocks + t / p->BS];
+  return widen(p->cache_dtype, p->v, v_index(b, g, t % p->BS, d, p->Hkv, p->D, p->BS)) * p->v_scale;
+}
+
+static int check_problem(const problem* p) {
+  if (p->S < 0 || p->Hq <= 0 || p->Hkv <= 0 || p->Hq % p->Hkv) return OR_INVALID;
+  if (p->D <= 0 || p->BS <= 0 || p->max_blocks < 0) return OR_INVALID;
+  if (elem_bytes(p->cache_dtype) == 0 || p->D % (16 / elem_bytes(p->cache_dtype))) return OR_INVALID;
+  if (p->q_dtype != OR_F32 && p->q_dtype != OR_BF16) return OR_INVALID;
+  for (int s = 0; s < p->S; ++s)
+    if (p->lens[s] < 0 || p->lens[s] > p->max_blocks * p->BS) return OR_INVALID;
+  return OR_OK;
+}
+
+/* Unsplit attention.  weights (nullable) receives w_t at [s][h][t] with row
+ * stride weights_stride (>= max L_s). */
+int oracle_decode_attention(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                            int block_size, int max_blocks_per_seq, int q_dtype, const void* q,
+                            int cache_dtype, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            float scale, float k_scale, float v_scale, double* out, double* lse,
+                            double* weights, int64_t weights_stride, int num_threads) {
+  problem p = {num_seqs,   num_q_heads, num_kv_heads, head_dim,     block_size,
+               max_blocks_per_seq, q_dtype, cache_dtype, q, k_cache, v_cache,
+               block_tables, context_lens, (double)scale, (double)k_scale, (double)v_scale};
+  int rc = check_problem(&p);
+  if (rc) return rc;
+  int G = num_q_heads / num_kv_heads;
+  int64_t pairs = (int64_t)num_seqs * num_q_heads;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int64_t i = 0; i < pairs; ++i) {
+    int s = (int)(i / num_q_heads), h = (int)(i % num_q_heads), g = h / G;
+    int L = context_lens[s];
+    double* o = out + i * head_dim;
+    for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
+    if (L == 0) {
+      lse[i] = -INFINITY;
+      continue;
+    }
+    double* sc = (double*)malloc(sizeof(double) * (size_t)L);
+    scores(&p, s, h, 0, L, sc);
+    double m = -INFINITY;
+    for (int t = 0; t < L; ++t)
+      if (sc[t] > m) m = sc[t];
+    double sum = 0.0;
+    for (int t = 0; t < L; ++t) sum += exp(sc[t] - m);
+    for (int t = 0; t < L; ++t) {
+      double w = exp(sc[t] - m) / sum;
+      if (weights) weights[i * weights_stride + t] = w;
+      for (int d = 0; d < head_dim; ++d) o[d] += w * v_at(&p, s, g, t, d);
+    }
+    lse[i] = m + log(sum);
+    free(sc);
+  }
+  return OR_OK;
+}
+
+/* Split-KV form: the tokens of a sequence are cut into partitions of
+ * partition_tokens; each partition p keeps (m_p, l_p = sum exp(sc - m_p),
+ * o_p = sum exp(sc - m_p) v); the partitions are merged with
+ * M = max m_p, Lambda = sum l_p e^{m_p - M}, out = sum e^{m_p - M} o_p / Lambda,
+ * lse = M + ln Lambda.  Exactly equal to the unsplit form in real arithmetic. */
+int oracle_decode_attention_split(int num_seqs, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int block_size, int max_blocks_per_seq,
+                                  int q_dtype, const void* q, int cache_dtype,
+                                  const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  float scale, float k_scale, float v_scale,
+                                  int partition_tokens, double* out, double* lse,
+                                  int num_threads) {
+  problem p = {num_seqs,   num_q_heads, num_kv_heads, head_dim,     block_size,
+               max_blocks_per_seq, q_dtype, cache_dtype, q, k_cache, v_cache,
+               block_tables, context_lens, (double)scale, (double)k_scale, (double)v_scale};
+  int rc = check_problem(&p);
+  if (rc) return rc;
+  if (partition_tokens <= 0) return OR_INVALID;
+  int G = num_q_heads / num_kv_heads;
+  int64_t pairs = (int64_t)num_seqs * num_q_heads;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int64_t i = 0; i < pairs; ++i) {
+    int s = (int)(i / num_q_heads), h = (int)(i % num_q_heads), g = h / G;
+    int L = context_lens[s];
+    double* o = out + i * head_dim;
+    for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
+    if (L == 0) {
+      lse[i] = -INFINITY;
+      continue;
+    }
+    int P = (L + partition_tokens - 1) / partition_tokens;
+    double* mp = (double*)malloc(sizeof(double) * (size_t)P);
+    double* lp = (double*)malloc(sizeof(double) * (size_t)P);
+    double* op = (double*)calloc((size_t)P * (size_t)head_dim, sizeof(double));
+    double* sc = (double*)malloc(sizeof(double) * (size_t)partition_tokens);
+    for (int part = 0; part < P; ++part) {
+      int t0 = part * partition_tokens;
+      int t1 = t0 + partition_tokens < L ? t0 + partition_tokens : L;
+      scores(&p, s, h, t0, t1, sc);
+      double m = -INFINITY;
+      for (int t = t0; t < t1; ++t)
+        if (sc[t - t0] > m) m = sc[t - t0];
+      double l = 0.0;
+      for (int t = t0; t < t1; ++t) {
+        double e = exp(sc[t - t0] - m);
+        l += e;
+        for (int d = 0; d < head_dim; ++d) op[(int64_t)part * head_dim + d] += e * v_at(&p, s, g, t, d);
+      }
+      mp[part] = m;
+      lp[part] = l;
+    }
+    double M = -INFINITY;
+    for (int part = 0; part < P; ++part)
+      if (mp[part] > M) M = mp[part];
+    double Lam = 0.0;
+    for (int part = 0; part < P; ++part) Lam += lp[part] * exp(mp[part] - M);
+    for (int part = 0; part < P; ++part) {
+      double c = exp(mp[part] - M) / Lam;
+      for (int d = 0; d < head_dim; ++d) o[d] += c * op[(int64_t)part * head_dim + d];
+    }
+    lse[i] = M + log(Lam);
+    free(mp);
+    free(lp);
+    free(op);
+    free(sc);
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Block allocation ([P1] PagedAttention Mechanics: a new token is appended  */
+/* to its sequence and a physical page is taken only when the sequence needs */
+/* one; several sequences may point at the same physical pages; [P4] §4:    */
+/* a finished request's blocks are freed at once).                          */
+/*                                                                            */
+/* Reading of what the pages leave open: free blocks form a FIFO queue seeded */
+/* with a given order; a block is taken from the head when a token's         */
+/* position p has p % BS == 0; a block whose reference count drops to 0 goes */
+/* to the tail.  slot = table[p / BS] * BS + p % BS.  An append list either  */
+/* succeeds whole or changes nothing.  Appending into a partially filled     */
+/* block that another sequence also references is refused (SHARED_TAIL).     */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t id;
+  int32_t len;
+  int32_t* table; /* max_blocks entries */
+} or_seq;
+
+typedef struct {
+  int num_blocks, BS, max_blocks;
+  int32_t* fifo; /* ring of num_blocks entries */
+  int head, count;
+  int32_t* ref;
+  or_seq* seqs;
+  int nseq, cap;
+} oracle_bm;
+
+oracle_bm* oracle_bm_create(int num_blocks, int block_size, int max_blocks_per_seq,
+                            const int32_t* free_order) {
+  if (num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq <= 0) return NULL;
+  oracle_bm* bm = (oracle_bm*)calloc(1, sizeof(oracle_bm));
+  bm->num_blocks = num_blocks;
+  bm->BS = block_size;
+  bm->max_blocks = max_blocks_per_seq;
+  bm->fifo = (int32_t*)malloc(sizeof(int32_t) * (size_t)num_blocks);
+  bm->ref = (int32_t*)calloc((size_t)num_blocks, sizeof(int32_t));
+  for (int i = 0; i < num_blocks; ++i) bm->fifo[i] = free_order ? free_order[i] : i;
+  bm->head = 0;
+  bm->count = num_blocks;
+  return bm;
+}
+
+void oracle_bm_destroy(oracle_bm* bm) {
+  if (!bm) return;
+  for (int i = 0; i < bm->nseq; ++i) free(bm->seqs[i].table);
+  free(bm->seqs);
+  free(bm->fifo);
+  free(bm->ref);
+  free(bm);
+}
+
+static int find_seq(const oracle_bm* bm, int64_t id) {
+  for (int i = 0; i < bm->nseq; ++i)
+    if (bm->seqs[i].id == id) return i;
+  return -1;
+}
+
+static int new_seq(oracle_bm* bm, int64_t id) {
+  if (bm->nseq == bm->cap) {
+    bm->cap = bm->cap ? 2 * bm->cap : 16;
+    bm->seqs = (or_seq*)realloc(bm->seqs, sizeof(or_seq) * (size_t)bm->cap);
+  }
+  or_seq* q = &bm->seqs[bm->nseq];
+  q->id = id;
+  q->len = 0;
+  q->table = (int32_t*)malloc(sizeof(int32_t) * (size_t)bm->max_blocks);
+  for (int i = 0; i < bm->max_blocks; ++i) q->table[i] = -1;
+  return bm->nseq++;
+}
+
+int oracle_bm_add_seq(oracle_bm* bm, int64_t id) {
+  if (find_seq(bm, id) >= 0) return OR_SEQ_EXISTS;
+  new_seq(bm, id);
+  return OR_OK;
+}
+
+int oracle_bm_fork_seq(oracle_bm* bm, int64_t parent, int64_t child) {
+  int pi = find_seq(bm, parent);
+  if (pi < 0) return OR_UNKNOWN_SEQ;
+  if (find_seq(bm, child) >= 0) return OR_SEQ_EXISTS;
+  int ci = new_seq(bm, child);
+  or_seq* P = &bm->seqs[pi]; /* re-read: new_seq may move the array */
+  or_seq* C = &bm->seqs[ci];
+  int nb = (P->len + bm->BS - 1) / bm->BS;
+  C->len = P->len;
+  for (int i = 0; i < nb; ++i) {
+    C->table[i] = P->table[i];
+    bm->ref[P->table[i]] += 1;
+  }
+  return OR_OK;
+}
+
+int oracle_bm_append_slots(oracle_bm* bm, const int64_t* ids, int n, int64_t* slots) {
+  /* dry run on copies of the lengths: validate and count new blocks */
+  int need = 0;
+  int32_t* lens = (int32_t*)malloc(sizeof(int32_t) * (size_t)(bm->nseq + 1));
+  for (int i = 0; i < bm->nseq; ++i) lens[i] = bm->seqs[i].len;
+  int rc = OR_OK;
+  for (int k = 0; k < n && rc == OR_OK; ++k) {
+    int i = find_seq(bm, ids[k]);
+    if (i < 0) {
+      rc = OR_UNKNOWN_SEQ;
+      break;
+    }
+    int p = lens[i];
+    if (p / bm->BS >= bm->max_blocks) {
+      rc = OR_INVALID;
+      break;
+    }
+    if (p % bm->BS == 0) {
+      need += 1;
+    } else if (p == bm->seqs[i].len && bm->ref[bm->seqs[i].table[p / bm->BS]] > 1) {
+      rc = OR_SHARED_TAIL;
+      break;
+    }
+    lens[i] = p + 1;
+  }
+  free(lens);
+  if (rc != OR_OK) return rc;
+  if (need > bm->count) return OR_OUT_OF_BLOCKS;
+  for (int k = 0; k < n; ++k) {
+    or_seq* q = &bm->seqs[find_seq(bm, ids[k])];
+    int p = q->len;
+    if (p % bm->BS == 0) {
+      int32_t blk = bm->fifo[bm->head];
+      bm->head = (bm->head + 1) % bm->num_blocks;
+      bm->count -= 1;
+      bm->ref[blk] = 1;
+      q->table[p / bm->BS] = blk;
+    }
+    slots[k] = (int64_t)q->table[p / bm->BS] * bm->BS + p % bm->BS;
+    q->len = p + 1;
+  }
+  return OR_OK;
+}
+
+int oracle_bm_free_seq(oracle_bm* bm, int64_t id) {
+  int i = find_seq(bm, id);
+  if (i < 0) return OR_UNKNOWN_SEQ;
+  or_seq* q = &bm->seqs[i];
+  int nb = (q->len + bm->BS - 1) / bm->BS;
+  for (int j = 0; j < nb; ++j) {
+    int32_t blk = q->table[j];
+    bm->ref[blk] -= 1;
+    if (bm->ref[blk] == 0) {
+      bm->fifo[(bm->head + bm->count) % bm->num_blocks] = blk;
+      bm->count += 1;
+    }
+  }
+  free(q->table);
+  bm->seqs[i] = bm->seqs[bm->nseq - 1];
+  bm->nseq -= 1;
+  return OR_OK;
+}
+
+int oracle_bm_export(const oracle_bm* bm, const int64_t* ids, int n, int32_t* tables,
+                     int32_t* lens) {
+  for (int k = 0; k < n; ++k) {
+    int i = find_seq(bm, ids[k]);
+    if (i < 0) return OR_UNKNOWN_SEQ;
+    const or_seq* q = &bm->seqs[i];
+    int nb = (q->len + bm->BS - 1) / bm->BS;
+    for (int j = 0; j < bm->max_blocks; ++j) tables[(int64_t)k * bm->max_blocks + j] = j < nb ? q->table[j] : -1;
+    lens[k] = q->len;
+  }
+  return OR_OK;
+}
+
+int oracle_bm_num_free(const oracle_bm* bm) { return bm->count; }
+
+int oracle_bm_refcount(const oracle_bm* bm, int block) {
+  if (block < 0 || block >= bm->num_blocks) return -1;
+  return bm->ref[block];
+}
