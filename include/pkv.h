@@ -1,0 +1,241 @@
+/*
+ * pkv.h -- C ABI of a paged KV-cache decode-attention library for AMD MI355X
+ * (gfx950).
+ *
+ * The calls follow how the pages state the problem.  Page titles, cited by
+ * section below:
+ *  [P1] "Optimizing Llama 3.1 405B Inference with vLLM PagedAttention"
+ *  [P2] "Optimizing vLLM Throughput with PagedAttention and Continuous
+ *       Batching for Llama 3"
+ *  [P3] "vLLM PagedAttention Optimization: Complete Step-by-Step Tuning Guide
+ *       for Low-Latency Inference"
+ *  [P4] "vLLM PagedAttention: Memory Optimization & High-Throughput LLM
+ *       Inference Tuning"
+ *
+ * What the calls cover:
+ *  - a pool of fixed-size physical blocks of 16 tokens ([P1] "Why Standard
+ *    Attention Fails at Scale"; [P4] §2);
+ *  - a block table per sequence, mapping logical to physical blocks ([P1]
+ *    "PagedAttention Mechanics"; [P3] "How PagedAttention Solves the KV Cache
+ *    Bottleneck"; [P4] §2);
+ *  - appending a token, which takes a physical block only when the sequence
+ *    needs a new one ([P1] "PagedAttention Mechanics");
+ *  - sharing of physical blocks between sequences with a common prefix ([P1]
+ *    "PagedAttention Mechanics"; [P4] §2);
+ *  - freeing a finished request's blocks ([P4] §4);
+ *  - the cache write of each new token's K and V, and decode attention that
+ *    walks the block table ([P4] §2).
+ *
+ * Conventions shared by every call:
+ *  - No call throws.  Each returns a pkv_status; pkv_last_error() gives
+ *    the text of the calling thread's last failure.
+ *  - Host pointers are read or written only during the call.
+ *  - Device pointers are caller-owned device memory.  The library never
+ *    allocates or frees device memory.  Device operations are enqueued on
+ *    `stream` (a hipStream_t; NULL = the null stream), never synchronise,
+ *    and their buffers must outlive the enqueued work.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    rejected call enqueues nothing.
+ *  - dtype codes: PKV_F32 (IEEE binary32), PKV_BF16 (bfloat16 bit
+ *    patterns), PKV_FP8_E4M3 (OCP E4M3FN codes: bias 7, no infinities,
+ *    S.1111.111 = NaN, largest finite 448; [P1] "Quantization Without
+ *    Quality Loss" and [P3] Step 3 name E4M3).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,
+  PKV_ERR_OUT_OF_BLOCKS = -2, /* the pool has too few free blocks ("KV cache full", [P2]) */
+  PKV_ERR_UNKNOWN_SEQ = -3,
+  PKV_ERR_SEQ_EXISTS = -4,
+  PKV_ERR_SHARED_TAIL = -5,   /* append into a partially filled block another sequence shares */
+  PKV_ERR_UNSUPPORTED = -6,   /* valid request outside the compiled kernel variants */
+  PKV_ERR_HIP = -7            /* the HIP runtime reported an error (text in pkv_last_error) */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
+
+/* ======================================================================== */
+/* Host block manager                                                        */
+/* ======================================================================== */
+/* Owns host memory only.  Not thread-safe: one scheduler thread drives it.
+ *
+ * Allocation policy (the pages leave it open): free blocks form a FIFO queue
+ * seeded with `free_order`; a token at position p of a sequence takes the
+ * block at the head of the queue when p % block_size == 0 ([P1] "PagedAttention
+ * Mechanics": a page is taken only when needed); its slot is
+ * table[p / block_size] * block_size + p % block_size.  Reference counts track
+ * sharing; a block whose count reaches 0 is appended to the queue tail, in
+ * the order the freed sequence's table held it. */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* num_blocks > 0 physical blocks of block_size tokens; each table holds
+ * max_blocks_per_seq entries.  free_order: NULL for 0..num_blocks-1, else a
+ * permutation of 0..num_blocks-1 (copied).  *out receives the handle. */
+pkv_status pkv_bm_create(int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                         const int32_t* free_order, pkv_block_manager** out);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* A new, empty sequence.  SEQ_EXISTS if the id is live. */
+pkv_status pkv_bm_add_seq(pkv_block_manager* bm, int64_t seq_id);
+
+/* A new sequence `child` holding the same tokens as `parent`: its table
+ * points at the parent's physical blocks, whose reference counts grow by one
+ * (prefix sharing, [P1] "PagedAttention Mechanics"; [P4] §2). */
+pkv_status pkv_bm_fork_seq(pkv_block_manager* bm, int64_t parent, int64_t child);
+
+/* Appends one token to each listed sequence, in list order (an id may
+ * appear several times: one token each), writing each token's slot to
+ * slot_mapping_out[i] (n entries, host memory).  All or nothing: on any
+ * error no state changes.  Errors: UNKNOWN_SEQ, INVALID_ARG (a table would
+ * outgrow max_blocks_per_seq), SHARED_TAIL, OUT_OF_BLOCKS. */
+pkv_status pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                               int64_t* slot_mapping_out);
+
+/* Drops the sequence; each of its blocks loses one reference ([P4] §4). */
+pkv_status pkv_bm_free_seq(pkv_block_manager* bm, int64_t seq_id);
+
+/* Writes, for the n listed sequences, their tables into block_tables_out
+ * (n x max_blocks_per_seq int32, row-major; entries past the last used block
+ * are -1) and their token counts into context_lens_out (n int32). */
+pkv_status pkv_bm_export(const pkv_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                         int32_t* block_tables_out, int32_t* context_lens_out);
+
+int32_t pkv_bm_num_free_blocks(const pkv_block_manager* bm);
+/* Reference count of a physical block (-1 if out of range). */
+int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);
+
+/* ======================================================================== */
+/* Device memory layout                                                      */
+/* ======================================================================== */
+/* The pages fix no layout; this library's is:
+ *   q, out        [num_seqs][num_q_heads][head_dim]
+ *   k_new, v_new  [num_tokens][num_kv_heads][head_dim]
+ *   k_cache       [num_blocks][num_kv_heads][head_dim / X][block_size][X],
+ *                 X = 16 bytes / element size (f32 4, bf16 8, fp8 16)
+ *   v_cache       [num_blocks][num_kv_heads][head_dim][block_size]
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32
+ *   context_lens  [num_seqs] int32
+ *   slot_mapping  [num_tokens] int64, slot = block * block_size + offset
+ * One (block, kv head) K tile keeps 16 bytes of one token's K contiguous,
+ * tokens next; the V tile keeps one dimension's 16 token values contiguous.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads). */
+
+/* ======================================================================== */
+/* Cache write                                                               */
+/* ======================================================================== */
+/* Writes each new token's K and V into the slot slot_mapping[i] names ([P1]
+ * "PagedAttention Mechanics": a new token is appended to its sequence).
+ *   src_dtype  : PKV_F32 or PKV_BF16 (k_new, v_new)
+ *   cache_dtype: PKV_F32 (src f32 only), PKV_BF16, PKV_FP8_E4M3
+ * Values are copied bit for bit when the dtypes match, rounded to nearest
+ * even for f32 -> bf16, and for fp8 stored as the satfinite round-to-nearest-
+ * even E4M3 code of the fp32 quotient x / scale (k_scale for K, v_scale for
+ * V; both > 0).  A slot < 0, or >= num_blocks * block_size, is skipped.
+ * Two tokens with one slot race (the block manager never issues that).
+ * head_dim in {64, 128}, block_size == 16. */
+pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype src_dtype,
+                                 void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                                 const int64_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int64_t num_blocks, float k_scale, float v_scale, void* stream);
+
+/* ======================================================================== */
+/* Decode attention over the paged cache                                     */
+/* ======================================================================== */
+/* For each sequence s and query head h (g = h / G, G = Hq / Hkv), over the
+ * L_s = context_lens[s] tokens whose K and V the table reaches ([P4] §1: the
+ * next token attends to every earlier token; [P4] §2: the kernel fetches
+ * K and V by walking the block table):
+ *   sc_t = scale * k_scale * q[s][h] . K_t
+ *   out[s][h] = sum_t softmax(sc)_t * v_scale * V_t,  lse[s][h] = ln sum_t e^{sc_t}
+ * The softmax is evaluated with a running maximum.  Long contexts are cut
+ * into partitions of partition_size tokens, each attended independently,
+ * then merged by log-sum-exp (split-KV).  L_s == 0 yields a zero row and
+ * lse = -inf.
+ *
+ * Supported (q, cache, out) dtypes: (F32, F32, F32), (BF16, BF16, BF16),
+ * (BF16, FP8_E4M3, BF16).  head_dim in {64, 128}; block_size 16;
+ * 1 <= Hq / Hkv <= 16; partition_size = 0 picks a default, else a positive
+ * multiple of block_size.  context_lens must lie in [0, max_context_len] and
+ * max_context_len <= max_blocks_per_seq * block_size; table entries of the
+ * first ceil(L_s / 16) columns must be < num_blocks.  Other entries and slots
+ * past L_s are never read (they may hold anything, NaN included).  Out-of-
+ * range lengths are clamped and out-of-range block ids are clamped into the
+ * pool, so a bad input never reads outside the buffers; its output is then
+ * unspecified. */
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;
+  int32_t partition_size; /* tokens per split-KV partition; 0 = default */
+  int64_t num_blocks;
+  float scale;            /* usually 1/sqrt(head_dim) */
+  float k_scale;          /* dequant scale of the K cache (1 unless fp8) */
+  float v_scale;
+  int32_t q_dtype;        /* pkv_dtype */
+  int32_t cache_dtype;
+  int32_t out_dtype;
+} pkv_decode_params;
+
+/* Bytes of device workspace pkv_decode_attention needs for these params
+ * (0 when no sequence can span more than one partition).  The workspace
+ * holds per-partition fp32 partial results; it need not be initialised. */
+size_t pkv_decode_workspace_bytes(const pkv_decode_params* p);
+
+/* The partition size (tokens) the call will use for these params. */
+int32_t pkv_decode_partition_size(const pkv_decode_params* p);
+
+/* Both passes: per-partition attention, then the log-sum-exp merge.
+ * out: [S][Hq][D] of out_dtype.  lse_out: NULL or [S][Hq] fp32.
+ * workspace: device memory of at least pkv_decode_workspace_bytes(p). */
+pkv_status pkv_decode_attention(const pkv_decode_params* p, void* out, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                void* workspace, size_t workspace_bytes, float* lse_out,
+                                void* stream);
+
+/* Pass 1 alone: every (sequence, kv head, partition) attends to its
+ * partition's tokens.  A sequence that fits one partition gets its final
+ * out / lse here; longer ones leave fp32 partials in the workspace. */
+pkv_status pkv_decode_attention_partitions(const pkv_decode_params* p, void* out, const void* q,
+                                           const void* k_cache, const void* v_cache,
+                                           const int32_t* block_tables,
+                                           const int32_t* context_lens, void* workspace,
+                                           size_t workspace_bytes, float* lse_out, void* stream);
+
+/* Pass 2 alone: merges the partials pass 1 left for sequences longer than
+ * one partition: M = max_p m_p, Lambda = sum_p l_p e^{m_p - M},
+ * out = sum_p e^{m_p - M} o_p / Lambda, lse = M + ln Lambda.  Enqueues
+ * nothing when no sequence can span two partitions. */
+pkv_status pkv_decode_attention_merge(const pkv_decode_params* p, void* out,
+                                      const int32_t* context_lens, const void* workspace,
+                                      size_t workspace_bytes, float* lse_out, void* stream);
+
+/* ======================================================================== */
+/* Diagnostics                                                               */
+/* ======================================================================== */
+const char* pkv_status_string(pkv_status s);
+/* Text of the calling thread's last failed call ("" if none). */
+const char* pkv_last_error(void);
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -191,9 +191,12 @@ class BlockAllocator:
             raise ValueError("oracle_bm_create failed")
 
     def __del__(self):
-        if getattr(self, "h", None):
-            lib().oracle_bm_destroy(self.h)
-            self.h = None
+        try:
+            if getattr(self, "h", None):
+                lib().oracle_bm_destroy(self.h)
+                self.h = None
+        except Exception:  # interpreter shutdown
+            pass
 
     def add_seq(self, sid):
         return lib().oracle_bm_add_seq(self.h, sid)

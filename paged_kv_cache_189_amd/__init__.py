@@ -1,0 +1,282 @@
+"""Python binding of libpkv (include/pkv.h): paged KV-cache decode attention
+for AMD MI355X (gfx950).
+
+Argument marshalling only.  Every function keeps its C name; tensors are
+passed as ``data_ptr()`` plus their dtype code, and device calls are
+enqueued on torch's current HIP stream unless a stream is given.  Nothing
+here computes: all device work runs in the HIP kernels of libpkv.so, and a
+missing library raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = -1
+PKV_ERR_OUT_OF_BLOCKS = -2
+PKV_ERR_UNKNOWN_SEQ = -3
+PKV_ERR_SEQ_EXISTS = -4
+PKV_ERR_SHARED_TAIL = -5
+PKV_ERR_UNSUPPORTED = -6
+PKV_ERR_HIP = -7
+
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+
+# every symbol include/pkv.h declares
+EXPORTED = (
+    "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_seq", "pkv_bm_fork_seq",
+    "pkv_bm_append_slots", "pkv_bm_free_seq", "pkv_bm_export", "pkv_bm_num_free_blocks",
+    "pkv_bm_refcount", "pkv_reshape_and_cache", "pkv_decode_workspace_bytes",
+    "pkv_decode_partition_size", "pkv_decode_attention", "pkv_decode_attention_partitions",
+    "pkv_decode_attention_merge", "pkv_status_string", "pkv_last_error", "pkv_version",
+)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = ""
+        try:
+            msg = _lib.pkv_last_error().decode()
+        except Exception:
+            pass
+        super().__init__(f"{where}: {_status_name(status)} ({status}): {msg}")
+
+
+class pkv_decode_params(C.Structure):
+    _fields_ = [
+        ("num_seqs", C.c_int32), ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+        ("head_dim", C.c_int32), ("block_size", C.c_int32), ("max_blocks_per_seq", C.c_int32),
+        ("max_context_len", C.c_int32), ("partition_size", C.c_int32), ("num_blocks", C.c_int64),
+        ("scale", C.c_float), ("k_scale", C.c_float), ("v_scale", C.c_float),
+        ("q_dtype", C.c_int32), ("cache_dtype", C.c_int32), ("out_dtype", C.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libpkv.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_189_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        P, I32, I64, F = C.c_void_p, C.c_int32, C.c_int64, C.c_float
+        st = C.c_int
+        sig = {
+            "pkv_bm_create": (st, [I32, I32, I32, P, C.POINTER(P)]),
+            "pkv_bm_destroy": (None, [P]),
+            "pkv_bm_add_seq": (st, [P, I64]),
+            "pkv_bm_fork_seq": (st, [P, I64, I64]),
+            "pkv_bm_append_slots": (st, [P, P, I32, P]),
+            "pkv_bm_free_seq": (st, [P, I64]),
+            "pkv_bm_export": (st, [P, P, I32, P, P]),
+            "pkv_bm_num_free_blocks": (I32, [P]),
+            "pkv_bm_refcount": (I32, [P, I32]),
+            "pkv_reshape_and_cache": (st, [P, P, st, P, P, st, P, I32, I32, I32, I32, I64, F, F, P]),
+            "pkv_decode_workspace_bytes": (C.c_size_t, [C.POINTER(pkv_decode_params)]),
+            "pkv_decode_partition_size": (I32, [C.POINTER(pkv_decode_params)]),
+            "pkv_decode_attention": (st, [C.POINTER(pkv_decode_params), P, P, P, P, P, P, P,
+                                          C.c_size_t, P, P]),
+            "pkv_decode_attention_partitions": (st, [C.POINTER(pkv_decode_params), P, P, P, P, P,
+                                                     P, P, C.c_size_t, P, P]),
+            "pkv_decode_attention_merge": (st, [C.POINTER(pkv_decode_params), P, P, P, C.c_size_t,
+                                                P, P]),
+            "pkv_status_string": (C.c_char_p, [st]),
+            "pkv_last_error": (C.c_char_p, []),
+            "pkv_version": (C.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return lib().pkv_status_string(s).decode()
+    except Exception:
+        return str(s)
+
+
+def _check(status: int, where: str):
+    if status != PKV_OK:
+        raise PkvError(status, where)
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return PKV_F32
+    if t == torch.bfloat16:
+        return PKV_BF16
+    if t in (torch.uint8, torch.float8_e4m3fn):
+        return PKV_FP8_E4M3
+    raise TypeError(f"no pkv dtype for {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("pkv arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    for t in tensors:
+        if t is not None and t.is_cuda:
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+# ------------------------------------------------------------------ block manager
+class BlockManager:
+    """The host block manager (pkv_bm_*): tables, refcounts, FIFO free list."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_blocks_per_seq: int,
+                 free_order: Optional[np.ndarray] = None):
+        h = C.c_void_p()
+        fo = None
+        if free_order is not None:
+            fo_arr = np.ascontiguousarray(free_order, dtype=np.int32)
+            fo = fo_arr.ctypes.data
+        _check(lib().pkv_bm_create(num_blocks, block_size, max_blocks_per_seq, fo, C.byref(h)),
+               "pkv_bm_create")
+        self.h = h
+        self.block_size = block_size
+        self.max_blocks = max_blocks_per_seq
+        self.num_blocks = num_blocks
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().pkv_bm_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
+
+    # raw status codes (the allocation recipe and the tests read them)
+    def add_seq(self, seq_id: int) -> int:
+        return lib().pkv_bm_add_seq(self.h, seq_id)
+
+    def fork_seq(self, parent: int, child: int) -> int:
+        return lib().pkv_bm_fork_seq(self.h, parent, child)
+
+    def append_slots(self, seq_ids, out: Optional[np.ndarray] = None):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        slots = out if out is not None else np.empty(ids.shape, dtype=np.int64)
+        rc = lib().pkv_bm_append_slots(self.h, ids.ctypes.data, ids.size, slots.ctypes.data)
+        return rc, slots
+
+    def free_seq(self, seq_id: int) -> int:
+        return lib().pkv_bm_free_seq(self.h, seq_id)
+
+    def export(self, seq_ids, tables: Optional[np.ndarray] = None,
+               lens: Optional[np.ndarray] = None):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        if tables is None:
+            tables = np.empty((ids.size, self.max_blocks), dtype=np.int32)
+        if lens is None:
+            lens = np.empty(ids.size, dtype=np.int32)
+        rc = lib().pkv_bm_export(self.h, ids.ctypes.data, ids.size, tables.ctypes.data,
+                                 lens.ctypes.data)
+        return rc, tables, lens
+
+    def num_free(self) -> int:
+        return lib().pkv_bm_num_free_blocks(self.h)
+
+    def refcount(self, block: int) -> int:
+        return lib().pkv_bm_refcount(self.h, block)
+
+
+# ------------------------------------------------------------------ device ops
+def pkv_reshape_and_cache(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float = 1.0,
+                          v_scale: float = 1.0, stream=None):
+    """k_new, v_new: [T][Hkv][D]; caches in the pool layout; slot_mapping int64 [T]."""
+    T, Hkv, D = k_new.shape
+    _check(lib().pkv_reshape_and_cache(
+        _ptr(k_new), _ptr(v_new), dtype_code(k_new.dtype), _ptr(k_cache), _ptr(v_cache),
+        dtype_code(k_cache.dtype), _ptr(slot_mapping), T, Hkv, D, 16, k_cache.shape[0],
+        float(k_scale), float(v_scale), _stream(stream, k_cache)), "pkv_reshape_and_cache")
+
+
+def make_decode_params(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
+                       max_context_len: int, scale: float, k_scale: float = 1.0,
+                       v_scale: float = 1.0, out_dtype: Optional[torch.dtype] = None,
+                       partition_size: int = 0) -> pkv_decode_params:
+    S, Hq, D = q.shape
+    p = pkv_decode_params()
+    p.num_seqs, p.num_q_heads, p.num_kv_heads, p.head_dim = S, Hq, k_cache.shape[1], D
+    p.block_size = 16
+    p.max_blocks_per_seq = block_tables.shape[1]
+    p.max_context_len = int(max_context_len)
+    p.partition_size = int(partition_size)
+    p.num_blocks = k_cache.shape[0]
+    p.scale, p.k_scale, p.v_scale = float(scale), float(k_scale), float(v_scale)
+    p.q_dtype = dtype_code(q.dtype)
+    p.cache_dtype = dtype_code(k_cache.dtype)
+    p.out_dtype = dtype_code(out_dtype if out_dtype is not None else q.dtype)
+    return p
+
+
+def pkv_decode_workspace_bytes(params: pkv_decode_params) -> int:
+    return int(lib().pkv_decode_workspace_bytes(C.byref(params)))
+
+
+def pkv_decode_partition_size(params: pkv_decode_params) -> int:
+    return int(lib().pkv_decode_partition_size(C.byref(params)))
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def pkv_decode_attention(params: pkv_decode_params, out: torch.Tensor, q: torch.Tensor,
+                         k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                         context_lens: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None, stream=None):
+    wp, wb = _ws(workspace)
+    _check(lib().pkv_decode_attention(
+        C.byref(params), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), wp, wb, _ptr(lse), _stream(stream, out)), "pkv_decode_attention")
+
+
+def pkv_decode_attention_partitions(params, out, q, k_cache, v_cache, block_tables,
+                                    context_lens, workspace=None, lse=None, stream=None):
+    wp, wb = _ws(workspace)
+    _check(lib().pkv_decode_attention_partitions(
+        C.byref(params), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), wp, wb, _ptr(lse), _stream(stream, out)),
+        "pkv_decode_attention_partitions")
+
+
+def pkv_decode_attention_merge(params, out, context_lens, workspace=None, lse=None, stream=None):
+    wp, wb = _ws(workspace)
+    _check(lib().pkv_decode_attention_merge(
+        C.byref(params), _ptr(out), _ptr(context_lens), wp, wb, _ptr(lse),
+        _stream(stream, out)), "pkv_decode_attention_merge")
+
+
+def pkv_version() -> str:
+    return lib().pkv_version().decode()

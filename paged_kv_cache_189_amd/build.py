@@ -1,0 +1,60 @@
+"""Builds libpkv.so, the HIP library behind include/pkv.h, for gfx950.
+
+Run as ``python -m paged_kv_cache_189_amd.build``.  The library lands next to
+this file and is what the Python binding loads.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libpkv.so")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # keep the compiler from emitting packed fp32 instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
+
+
+def _hipcc() -> str:
+    for c in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    with tempfile.TemporaryDirectory(prefix="pkv_build_") as tmp:
+        objs = []
+
+        def run(cmd):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+
+        kobj = os.path.join(tmp, "kernels.o")
+        run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kobj])
+        objs.append(kobj)
+        cobj = os.path.join(tmp, "capi.o")
+        run([hipcc, "-x", "hip", *HIP_FLAGS, "-c", os.path.join(CSRC, "capi.cpp"), "-o", cobj])
+        objs.append(cobj)
+        bobj = os.path.join(tmp, "block_manager.o")
+        run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "block_manager.cpp"), "-o", bobj])
+        objs.append(bobj)
+        out_tmp = LIB + ".tmp"
+        run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp])
+        os.replace(out_tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

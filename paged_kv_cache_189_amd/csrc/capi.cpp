@@ -1,0 +1,263 @@
+// C ABI of libpkv: argument validation, kernel dispatch, workspace sizing and
+// error reporting for the device operations declared in include/pkv.h.
+// Every check runs on the host before anything is enqueued.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int32_t kBlockSize = 16;
+constexpr int32_t kDefaultPartition = 512;
+constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kMaxMergeLds = 64 * 1024;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int elem_bytes(int32_t dt) {
+  return dt == PKV_F32 ? 4 : dt == PKV_BF16 ? 2 : dt == PKV_FP8_E4M3 ? 1 : 0;
+}
+
+struct Layout {
+  int32_t partition = 0;  // tokens
+  int32_t max_parts = 1;
+  size_t o_off = 0, m_off = 0, l_off = 0, e_off = 0, bytes = 0;
+};
+
+Layout layout_of(const pkv_decode_params& p) {
+  Layout L;
+  L.partition = p.partition_size > 0 ? p.partition_size : kDefaultPartition;
+  const int64_t mc = p.max_context_len > 0 ? p.max_context_len : 0;
+  L.max_parts = mc > L.partition ? (int32_t)((mc + L.partition - 1) / L.partition) : 1;
+  if (L.max_parts <= 1) return L;
+  const size_t rows = (size_t)p.num_seqs * (size_t)p.num_q_heads * (size_t)L.max_parts;
+  L.o_off = 0;
+  L.m_off = round_up(rows * (size_t)p.head_dim * sizeof(float), 256);
+  L.l_off = L.m_off + round_up(rows * sizeof(float), 256);
+  L.e_off = L.l_off + round_up(rows * sizeof(float), 256);
+  L.bytes = L.e_off + round_up(rows * sizeof(float), 256);
+  return L;
+}
+
+pkv_status check_decode(const pkv_decode_params* p) {
+  if (!p) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: params is NULL");
+  if (p->num_seqs < 0) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: num_seqs < 0");
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0 || p->num_q_heads % p->num_kv_heads)
+    return pkv_fail(PKV_ERR_INVALID_ARG, "decode: num_q_heads must be a positive multiple of num_kv_heads");
+  const int32_t G = p->num_q_heads / p->num_kv_heads;
+  if (G > 16) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: query heads per kv head must be <= 16");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: head_dim must be 64 or 128");
+  if (p->block_size != kBlockSize) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: block_size must be 16");
+  if (p->max_blocks_per_seq <= 0) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: max_blocks_per_seq must be > 0");
+  if (p->max_context_len < 0 || (int64_t)p->max_context_len > (int64_t)p->max_blocks_per_seq * kBlockSize)
+    return pkv_fail(PKV_ERR_INVALID_ARG, "decode: max_context_len must be in [0, max_blocks_per_seq * block_size]");
+  if (p->partition_size < 0 || p->partition_size % kBlockSize)
+    return pkv_fail(PKV_ERR_INVALID_ARG, "decode: partition_size must be 0 or a positive multiple of block_size");
+  if (p->num_blocks <= 0) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: num_blocks must be > 0");
+  if (!std::isfinite(p->scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale) || p->k_scale <= 0.f ||
+      p->v_scale <= 0.f)
+    return pkv_fail(PKV_ERR_INVALID_ARG, "decode: scale must be finite, k_scale and v_scale finite and > 0");
+  const bool combo = (p->q_dtype == PKV_F32 && p->cache_dtype == PKV_F32 && p->out_dtype == PKV_F32) ||
+                     (p->q_dtype == PKV_BF16 && p->cache_dtype == PKV_BF16 && p->out_dtype == PKV_BF16) ||
+                     (p->q_dtype == PKV_BF16 && p->cache_dtype == PKV_FP8_E4M3 && p->out_dtype == PKV_BF16);
+  if (!combo)
+    return pkv_fail(PKV_ERR_UNSUPPORTED,
+                    "decode: (q, cache, out) dtypes must be (f32,f32,f32), (bf16,bf16,bf16) or (bf16,fp8,bf16)");
+  const Layout L = layout_of(*p);
+  if (L.max_parts > kMaxGridY) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: too many partitions per sequence");
+  if ((int64_t)L.max_parts * (int64_t)sizeof(float) > kMaxMergeLds)
+    return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: too many partitions per sequence");
+  if ((int64_t)p->num_seqs * p->num_q_heads > INT32_MAX)
+    return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: num_seqs * num_q_heads too large");
+  return PKV_OK;
+}
+
+pkv_status check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return pkv_fail(PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+pkv_status build_args(const pkv_decode_params* p, void* out, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                      const void* workspace, size_t workspace_bytes, float* lse_out, bool need_q_cache,
+                      pkv::DecodeArgs* a, Layout* lay) {
+  pkv_status st = check_decode(p);
+  if (st != PKV_OK) return st;
+  const Layout L = layout_of(*p);
+  if (p->num_seqs > 0) {
+    if (!out || !context_lens) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: out and context_lens are required");
+    if (need_q_cache && (!q || !k_cache || !v_cache || !block_tables))
+      return pkv_fail(PKV_ERR_INVALID_ARG, "decode: q, k_cache, v_cache and block_tables are required");
+    if (!aligned(out, (uintptr_t)elem_bytes(p->out_dtype)) || !aligned(context_lens, 4) ||
+        (need_q_cache && (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+                          !aligned(block_tables, 4))) ||
+        (lse_out && !aligned(lse_out, 4)))
+      return pkv_fail(PKV_ERR_INVALID_ARG, "decode: q and the caches must be 16-byte aligned, other arrays element aligned");
+    if (L.bytes > 0) {
+      if (!workspace || workspace_bytes < L.bytes)
+        return pkv_fail(PKV_ERR_INVALID_ARG, "decode: workspace missing or smaller than pkv_decode_workspace_bytes()");
+      if (!aligned(workspace, 256)) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: workspace must be 256-byte aligned");
+    }
+  }
+  pkv::DecodeArgs& d = *a;
+  d.out = out;
+  d.q = q;
+  d.k_cache = k_cache;
+  d.v_cache = v_cache;
+  d.block_tables = block_tables;
+  d.context_lens = context_lens;
+  char* ws = static_cast<char*>(const_cast<void*>(workspace));
+  d.ws_o = L.bytes ? reinterpret_cast<float*>(ws + L.o_off) : nullptr;
+  d.ws_m = L.bytes ? reinterpret_cast<float*>(ws + L.m_off) : nullptr;
+  d.ws_l = L.bytes ? reinterpret_cast<float*>(ws + L.l_off) : nullptr;
+  d.ws_e = L.bytes ? reinterpret_cast<float*>(ws + L.e_off) : nullptr;
+  d.lse = lse_out;
+  d.num_blocks = p->num_blocks;
+  d.num_seqs = p->num_seqs;
+  d.num_q_heads = p->num_q_heads;
+  d.num_kv_heads = p->num_kv_heads;
+  d.group = p->num_q_heads / p->num_kv_heads;
+  d.max_blocks = p->max_blocks_per_seq;
+  d.max_context_len = p->max_context_len;
+  d.part_blocks = L.partition / kBlockSize;
+  d.max_parts = L.max_parts;
+  d.score_scale_log2 = (float)((double)p->scale * (double)p->k_scale * 1.4426950408889634);
+  d.v_scale = p->v_scale;
+  *lay = L;
+  return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status pkv_fail(pkv_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_OUT_OF_BLOCKS: return "out of blocks (KV cache full)";
+    case PKV_ERR_UNKNOWN_SEQ: return "unknown sequence";
+    case PKV_ERR_SEQ_EXISTS: return "sequence exists";
+    case PKV_ERR_SHARED_TAIL: return "append into a shared, partially filled block";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
+
+pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype src_dtype, void* k_cache,
+                                 void* v_cache, pkv_dtype cache_dtype, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int64_t num_blocks, float k_scale, float v_scale, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+    return pkv_fail(PKV_ERR_INVALID_ARG, "reshape_and_cache: bad sizes");
+  if (head_dim != 64 && head_dim != 128)
+    return pkv_fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache: head_dim must be 64 or 128");
+  if (block_size != kBlockSize) return pkv_fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache: block_size must be 16");
+  const bool combo = (src_dtype == PKV_F32 && (cache_dtype == PKV_F32 || cache_dtype == PKV_BF16 ||
+                                               cache_dtype == PKV_FP8_E4M3)) ||
+                     (src_dtype == PKV_BF16 && (cache_dtype == PKV_BF16 || cache_dtype == PKV_FP8_E4M3));
+  if (!combo) return pkv_fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache: unsupported (src, cache) dtypes");
+  if (cache_dtype == PKV_FP8_E4M3 &&
+      (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
+    return pkv_fail(PKV_ERR_INVALID_ARG, "reshape_and_cache: fp8 scales must be finite and > 0");
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)
+    return pkv_fail(PKV_ERR_INVALID_ARG, "reshape_and_cache: NULL pointer");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return pkv_fail(PKV_ERR_INVALID_ARG, "reshape_and_cache: K/V arrays must be 16-byte aligned");
+  pkv::CacheWriteArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.slot_mapping = slot_mapping;
+  a.num_blocks = num_blocks;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  bool ok = false;
+  hipError_t e = pkv::launch_cache_write(a, src_dtype, cache_dtype, head_dim, (hipStream_t)stream, &ok);
+  if (!ok) return pkv_fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache: no kernel variant");
+  return check_hip(e, "reshape_and_cache launch");
+}
+
+size_t pkv_decode_workspace_bytes(const pkv_decode_params* p) {
+  if (check_decode(p) != PKV_OK) return 0;
+  return layout_of(*p).bytes;
+}
+
+int32_t pkv_decode_partition_size(const pkv_decode_params* p) {
+  if (check_decode(p) != PKV_OK) return -1;
+  return layout_of(*p).partition;
+}
+
+pkv_status pkv_decode_attention_partitions(const pkv_decode_params* p, void* out, const void* q, const void* k_cache,
+                                           const void* v_cache, const int32_t* block_tables,
+                                           const int32_t* context_lens, void* workspace, size_t workspace_bytes,
+                                           float* lse_out, void* stream) {
+  pkv::DecodeArgs a;
+  Layout L;
+  pkv_status st = build_args(p, out, q, k_cache, v_cache, block_tables, context_lens, workspace, workspace_bytes,
+                             lse_out, true, &a, &L);
+  if (st != PKV_OK) return st;
+  bool ok = false;
+  hipError_t e = pkv::launch_decode_partitions(a, p->cache_dtype, p->head_dim, (hipStream_t)stream, &ok);
+  if (!ok) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: no kernel variant");
+  return check_hip(e, "decode partitions launch");
+}
+
+pkv_status pkv_decode_attention_merge(const pkv_decode_params* p, void* out, const int32_t* context_lens,
+                                      const void* workspace, size_t workspace_bytes, float* lse_out, void* stream) {
+  pkv::DecodeArgs a;
+  Layout L;
+  pkv_status st = build_args(p, out, nullptr, nullptr, nullptr, nullptr, context_lens, workspace, workspace_bytes,
+                             lse_out, false, &a, &L);
+  if (st != PKV_OK) return st;
+  bool ok = false;
+  hipError_t e = pkv::launch_decode_merge(a, p->out_dtype, p->head_dim, (hipStream_t)stream, &ok);
+  if (!ok) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: no merge kernel variant");
+  return check_hip(e, "decode merge launch");
+}
+
+pkv_status pkv_decode_attention(const pkv_decode_params* p, void* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                void* workspace, size_t workspace_bytes, float* lse_out, void* stream) {
+  pkv::DecodeArgs a;
+  Layout L;
+  pkv_status st = build_args(p, out, q, k_cache, v_cache, block_tables, context_lens, workspace, workspace_bytes,
+                             lse_out, true, &a, &L);
+  if (st != PKV_OK) return st;
+  bool ok = false;
+  hipError_t e = pkv::launch_decode_partitions(a, p->cache_dtype, p->head_dim, (hipStream_t)stream, &ok);
+  if (!ok) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: no kernel variant");
+  st = check_hip(e, "decode partitions launch");
+  if (st != PKV_OK) return st;
+  e = pkv::launch_decode_merge(a, p->out_dtype, p->head_dim, (hipStream_t)stream, &ok);
+  if (!ok) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: no merge kernel variant");
+  return check_hip(e, "decode merge launch");
+}
+
+}  // extern "C"

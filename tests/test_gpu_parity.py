@@ -1,0 +1,248 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Bars: slot mapping and cache bytes bit-exact; attention within 1e-5 of each
+row's largest |value| for fp32, 1e-2 max-abs for bf16 outputs, 3e-2 max-abs
+for fp8 KV; the oracle consumes exactly the stored (rounded / quantized)
+values the GPU consumed.  Every case prints its name before its GPU work.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_189_amd as pkv
+import workloads
+from oracle import oracle as O
+from tests import gpu_case as G
+
+pytestmark = pytest.mark.gpu
+
+BS = 16
+F32, BF16, E4M3 = workloads.F32, workloads.BF16, workloads.E4M3
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pkv.lib()  # fail loudly if the library is missing
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def full_parity(c, seqs=None, label=""):
+    """Cache write (bit-exact) and attention (tolerance) on the sampled seqs."""
+    seqs = np.arange(len(c.lens)) if seqs is None else np.asarray(seqs)
+    before = G.host_copy(c, seqs)
+    G.log(f"[{label}] cache write + decode on GPU")
+    G.run_cache_write(c)
+    G.run_decode(c)
+    torch.cuda.synchronize()
+    after = G.host_copy(c, seqs)
+    G.oracle_cache_write(c, before)
+    assert np.array_equal(G.bits(before.k), G.bits(after.k)), f"{label}: K cache bytes differ"
+    assert np.array_equal(G.bits(before.v), G.bits(after.v)), f"{label}: V cache bytes differ"
+    ref, rlse, secs = G.oracle_decode(c, before)
+    err = G.compare_out(c, seqs, ref, rlse, label)
+    G.log(f"[{label}] max err {err:.3e} (oracle {secs:.2f}s)")
+    return ref, rlse
+
+
+def small_spec(index, base, S, Hq, Hkv, D, lens, cache=None):
+    spec = G.spec_with(index, base=base, num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv,
+                       head_dim=D, lengths=G.fixed_lengths(lens), pool_blocks=None,
+                       prefix_tokens=0, max_model_len=0)
+    if cache is not None:
+        qd = F32 if cache == F32 else BF16
+        spec = dataclasses.replace(spec, cache_dtype=cache, q_dtype=qd, out_dtype=qd)
+    return spec
+
+
+# ------------------------------------------------------------------- configs at small size
+@pytest.mark.parametrize("part", [0, 16, 64])
+def test_tiny_fp32_config(part):
+    spec = workloads.SPECS[1]
+    c = G.build(spec, partition_size=part)
+    full_parity(c, label=f"tiny fp32 part={part}")
+
+
+RAGGED = [1, 15, 16, 17, 100, 511, 512, 513, 1500, 2049]
+
+
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+@pytest.mark.parametrize("part", [0, 64])
+def test_ragged_lengths(cache, part):
+    base = {F32: 1, BF16: 2, E4M3: 4}[cache]
+    spec = small_spec(200 + cache, base, len(RAGGED), 32, 8, 128, RAGGED, cache)
+    c = G.build(spec, partition_size=part)
+    full_parity(c, label=f"ragged dtype={cache} part={part}")
+
+
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
+def test_gqa_headdim_dtype_variants(cache, D, group):
+    Hkv = 2
+    lens = [3, 40, 257, 700]
+    spec = small_spec(300 + 10 * group + D // 64 + cache, 2, len(lens), Hkv * group, Hkv, D, lens,
+                      cache)
+    c = G.build(spec, partition_size=256)
+    full_parity(c, label=f"gqa G={group} D={D} dtype={cache}")
+
+
+def test_empty_sequence_row():
+    spec = small_spec(400, 2, 3, 8, 2, 128, [33, 5, 600])
+    c = G.build(spec, partition_size=64)
+    c.d_lens[1] = 0
+    G.log("[empty] decode with one zero-length sequence")
+    G.run_cache_write(c)
+    G.run_decode(c)
+    torch.cuda.synchronize()
+    out = c.out.float().cpu().numpy()
+    lse = c.lse.cpu().numpy()
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+    assert np.all(np.isfinite(out[[0, 2]]))
+
+
+def test_passes_separately_equal_composed():
+    spec = small_spec(401, 2, 4, 16, 4, 128, [700, 1200, 35, 2000])
+    c = G.build(spec, partition_size=128)
+    G.log("[two passes] composed call")
+    G.run_cache_write(c)
+    G.run_decode(c)
+    torch.cuda.synchronize()
+    o1, l1 = c.out.clone(), c.lse.clone()
+    c.out.fill_(float("nan"))
+    c.lse.fill_(float("nan"))
+    w = c.w
+    G.log("[two passes] partitions then merge")
+    pkv.pkv_decode_attention_partitions(c.params, c.out, w.q, w.k_cache, w.v_cache, c.d_tables,
+                                        c.d_lens, c.workspace, c.lse)
+    pkv.pkv_decode_attention_merge(c.params, c.out, c.d_lens, c.workspace, c.lse)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), c.out.view(torch.int16)) and torch.equal(l1, c.lse)
+
+
+# ------------------------------------------------------------------- invariants of paging
+@pytest.mark.parametrize("cache", [BF16, E4M3])
+def test_block_relabel_bit_identical(cache):
+    lens = [70, 300, 1025, 16]
+    spec = small_spec(500 + cache, 2, len(lens), 16, 2, 128, lens, cache)
+    c = G.build(spec, partition_size=256)
+    G.log(f"[relabel dtype={cache}] original placement")
+    G.run_cache_write(c)
+    G.run_decode(c)
+    torch.cuda.synchronize()
+    o1, l1 = c.out.clone(), c.lse.clone()
+    nb = c.w.num_blocks
+    pi = torch.from_numpy(np.random.default_rng(9).permutation(nb)).to(c.out.device)
+    k2 = torch.empty_like(c.w.k_cache)
+    v2 = torch.empty_like(c.w.v_cache)
+    k2[pi] = c.w.k_cache
+    v2[pi] = c.w.v_cache
+    t2 = c.d_tables.clone()
+    m = t2 >= 0
+    t2[m] = pi[t2[m].long()].int()
+    G.log(f"[relabel dtype={cache}] permuted placement")
+    pkv.pkv_decode_attention(c.params, c.out, c.w.q, k2, v2, t2, c.d_lens, c.workspace, c.lse)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), c.out.view(torch.int16))
+    assert torch.equal(l1, c.lse)
+
+
+def test_shared_prefix_equals_copied_bit_identical():
+    spec = dataclasses.replace(workloads.SPECS[3], index=600, num_seqs=8)
+    lens = workloads.lengths(spec, 8)
+    c = G.build(spec, lens=lens, partition_size=512)
+    G.log("[prefix] shared prefix blocks")
+    G.run_cache_write(c)
+    G.run_decode(c)
+    torch.cuda.synchronize()
+    o1, l1 = c.out.clone(), c.lse.clone()
+    # copies of the 64 prefix blocks for sequences 1.., appended past the pool
+    pre = spec.prefix_tokens // BS
+    S = len(lens)
+    w = c.w
+    shared = torch.from_numpy(c.tables[0, :pre].astype(np.int64)).to(w.k_cache.device)
+    k2 = torch.cat([w.k_cache] + [w.k_cache[shared]] * (S - 1))
+    v2 = torch.cat([w.v_cache] + [w.v_cache[shared]] * (S - 1))
+    t2 = c.tables.copy()
+    for s in range(1, S):
+        t2[s, :pre] = w.num_blocks + (s - 1) * pre + np.arange(pre)
+    p2 = pkv.make_decode_params(w.q, k2, c.d_tables, c.params.max_context_len, w.scale,
+                                w.k_scale, w.v_scale, c.out.dtype, 512)
+    G.log("[prefix] copied prefix blocks")
+    pkv.pkv_decode_attention(p2, c.out, w.q, k2, v2, torch.from_numpy(t2).to(c.out.device),
+                             c.d_lens, c.workspace, c.lse)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), c.out.view(torch.int16))
+    assert torch.equal(l1, c.lse)
+
+
+def test_constant_v_gives_constant_output():
+    """V == 1 in every used block: the output is exactly 1 (the weights that
+    multiply V are the ones the normaliser sums).  Unused blocks keep NaN."""
+    lens = [1, 17, 900, 4000]
+    spec = small_spec(700, 2, len(lens), 32, 8, 128, lens)
+    c = G.build(spec, partition_size=512)
+    G.run_cache_write(c)
+    used = np.unique(np.concatenate([c.tables[s, :-(-int(L) // BS)] for s, L in enumerate(c.lens)]))
+    c.w.v_cache[torch.from_numpy(used).to(c.out.device)] = 1.0
+    G.log("[V==1] decode")
+    G.run_decode(c)
+    torch.cuda.synchronize()
+    assert torch.all(c.out.float() == 1.0)
+
+
+# ------------------------------------------------------------------- cache write variants
+@pytest.mark.parametrize("src,dst", [(F32, F32), (BF16, BF16), (F32, BF16), (BF16, E4M3),
+                                     (F32, E4M3)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_cache_write_bit_exact(src, dst, D):
+    rng = np.random.default_rng(800 + 10 * src + dst)
+    T, H, nb = 37, 4, 20
+    X = 16 // workloads.ELEM_BYTES[dst]
+    sdt = torch.float32 if src == F32 else torch.bfloat16
+    kn = (torch.from_numpy(rng.standard_normal((T, H, D)).astype(np.float32)) * 3).to(sdt).cuda()
+    vn = (torch.from_numpy(rng.standard_normal((T, H, D)).astype(np.float32)) * 3).to(sdt).cuda()
+    kn[0, 0, :4] = torch.tensor([1e6, -1e6, 3e-9, 0.0])  # saturation, subnormal, zero
+    slots = rng.choice(nb * BS, size=T, replace=False).astype(np.int64)
+    slots[3] = -1
+    slots[5] = nb * BS + 7  # out of range: skipped
+    kshape, vshape = workloads.pool_shapes(nb, H, D, dst)
+    sto = workloads.TORCH_STORAGE[dst]
+    kc = torch.zeros(kshape, dtype=sto, device="cuda")
+    vc = torch.zeros(vshape, dtype=sto, device="cuda")
+    ks, vs = (0.0137, 0.0291) if dst == E4M3 else (1.0, 1.0)
+    G.log(f"[cache write {src}->{dst} D={D}]")
+    pkv.pkv_reshape_and_cache(kn, vn, kc, vc, torch.from_numpy(slots).cuda(), ks, vs)
+    torch.cuda.synchronize()
+    ko = np.zeros(kshape, dtype=G.np_storage(kc[:1]).dtype)
+    vo = np.zeros(vshape, dtype=ko.dtype)
+    sl = slots.copy()
+    sl[5] = -1  # the oracle would reject it; the library skips it
+    O.reshape_and_cache(G.np_storage(kn), G.np_storage(vn), src, ko, vo, dst, sl, BS, ks, vs)
+    assert np.array_equal(G.bits(G.np_storage(kc)), G.bits(ko))
+    assert np.array_equal(G.bits(G.np_storage(vc)), G.bits(vo))
+
+
+# ------------------------------------------------------------------- full sizes, sampled
+def sample_seqs(lens, k, seed):
+    order = np.argsort(lens)
+    pick = {int(order[0]), int(order[-1])}
+    rng = np.random.default_rng(seed)
+    while len(pick) < min(k, len(lens)):
+        pick.add(int(rng.integers(0, len(lens))))
+    return np.array(sorted(pick))
+
+
+@pytest.mark.parametrize("index,k", [(2, 64), (3, 24), (4, 8), (5, 2)])
+def test_full_size_config_sampled(index, k):
+    spec = workloads.SPECS[index]
+    G.log(f"[config {index}] building {spec.name}")
+    c = G.build(spec)
+    seqs = sample_seqs(c.lens, k, index)
+    full_parity(c, seqs, label=f"config {index} full size, {len(seqs)} sampled seqs")
+    del c
