@@ -1,0 +1,307 @@
+"""Benchmark of the paged decode-attention hot path on one MI355X.
+
+One step = one decode step of one attention layer over a batch of resident
+sequences, i.e. the whole hot path:
+  a1  host block manager appends one token per sequence (a block is taken
+      only at a block boundary) and exports slots, tables and lengths, which
+      are copied to the device (pinned, double-buffered, async);
+  a2  reshape_and_cache writes each new token's K and V into its slot;
+  a3-a8  decode attention: pass 1 (per-partition attention over the block
+      table) and pass 2 (log-sum-exp merge of split-KV partials).
+Inputs are resident in HBM before the timed region; each step decodes the
+next token, so contexts grow by one per step.
+
+Prints one JSON line.  `value` is KV GB/s over the whole step (algorithmic
+KV bytes / step time); `roofline` is the pass-1 kernel's algorithmic bytes
+per launch over its HIP-event-timed average duration, against 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: KV GB/s and % of HBM peak; seq-tokens/s per layer"
+HBM_PEAK_GBS = 8000.0
+BS = 16
+COUNTERS = os.path.join(ROOT, "profiles", "pass1_hbm_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_189_amd", "csrc", "kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload index (1-5)")
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="tokens per split-KV partition (-1: the workload's choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=0,
+                    help="sequences in the oracle sample (0: the default for the workload)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+# Partition sizes chosen per workload (tokens); 0 = library default.
+PARTITION = {1: 0, 2: 1024, 3: 1024, 4: 2048, 5: 512}
+CPU_SEQS = {1: 4, 2: 64, 3: 32, 4: 8, 5: 1}
+
+
+def kv_bytes(spec, tables, lens):
+    """Algorithmic KV bytes: tokens used in each UNIQUE physical block, times
+    2 (K and V) * kv heads * head dim * bytes per element; and the logical
+    figure that counts shared blocks once per sequence."""
+    import workloads
+    per_tok = 2 * spec.num_kv_heads * spec.head_dim * workloads.ELEM_BYTES[spec.cache_dtype]
+    lens = np.asarray(lens, dtype=np.int64)
+    n = (lens + BS - 1) // BS
+    cols = np.arange(tables.shape[1])[None, :]
+    mask = cols < n[:, None]
+    blocks = tables[mask].astype(np.int64)
+    used = np.minimum(BS, (lens[:, None] - cols * BS))[mask]
+    fill = np.zeros(int(blocks.max()) + 1 if blocks.size else 1, dtype=np.int64)
+    np.maximum.at(fill, blocks, used)
+    return int(fill.sum()) * per_tok, int(lens.sum()) * per_tok
+
+
+def other_bytes(spec, lens):
+    import workloads
+    S = len(lens)
+    qb = workloads.ELEM_BYTES[spec.q_dtype]
+    ob = workloads.ELEM_BYTES[spec.out_dtype]
+    tables = 4 * int(sum(-(-int(L) // BS) for L in lens))
+    return S * spec.num_q_heads * spec.head_dim * (qb + ob) + tables + 4 * S
+
+
+def copy_probe(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "launches": 3}), flush=True)
+
+
+def traffic_from_counters():
+    """HBM bytes per pass-1 launch from the committed rocprofv3 counter runs,
+    or None when the kernel source changed since they were taken."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        if c.get("kernels_hip_sha256") != src:
+            return None
+        return c
+    except (OSError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
+              "not sharded across GPUs in this library.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_189_amd as pkv
+    import workloads
+
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pkv.lib()
+    dev = torch.device("cuda:0")
+    spec = workloads.SPECS[args.config]
+    part = PARTITION[args.config] if args.partition < 0 else args.partition
+    total_steps = args.warmup + args.steps
+    lens0 = workloads.lengths(spec)
+    S = len(lens0)
+    t_build = time.perf_counter()
+    w = workloads.make(spec, device=dev, lens=lens0)
+    # table wide enough for the tokens this run appends
+    width = w.max_blocks * BS + total_steps + BS
+    max_blocks = -(-width // BS)
+    nb_extra = S * (-(-total_steps // BS) + 1)
+    # grow the pool for the appended tokens (fresh blocks hold N(0,1)-free garbage;
+    # they are written by the cache write before they are read)
+    if nb_extra:
+        ks, vs = workloads.pool_shapes(nb_extra, spec.num_kv_heads, spec.head_dim, spec.cache_dtype)
+        w.k_cache = torch.cat([w.k_cache, torch.zeros(ks, dtype=w.k_cache.dtype, device=dev)])
+        w.v_cache = torch.cat([w.v_cache, torch.zeros(vs, dtype=w.v_cache.dtype, device=dev)])
+    num_blocks = w.num_blocks + nb_extra
+    order = np.concatenate([w.free_order, np.arange(w.num_blocks, num_blocks, dtype=np.int32)])
+    bm = pkv.BlockManager(num_blocks, BS, max_blocks, order)
+    slots0 = workloads.allocate_context(bm, spec, lens0)  # context + first decode token
+    ids = np.arange(S, dtype=np.int64)
+    _, tables0, blens = bm.export(ids)
+    workloads.poison_unused(w, tables0[:, : w.max_blocks], lens0 - 1)
+
+    out_dtype = torch.float32 if spec.out_dtype == workloads.F32 else torch.bfloat16
+    d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device=dev)
+    d_lens = torch.empty(S, dtype=torch.int32, device=dev)
+    d_slots = torch.empty(S, dtype=torch.int64, device=dev)
+    params = pkv.make_decode_params(w.q, w.k_cache, d_tables, max_blocks * BS, w.scale, w.k_scale,
+                                    w.v_scale, out_dtype, part)
+    ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(params), 256), dtype=torch.uint8, device=dev)
+    out = torch.empty(w.q.shape, dtype=out_dtype, device=dev)
+    lse = torch.empty((S, spec.num_q_heads), dtype=torch.float32, device=dev)
+    # two pinned host buffer sets for the per-step metadata
+    pin = [dict(slots=torch.empty(S, dtype=torch.int64, pin_memory=True),
+                tables=torch.empty((S, max_blocks), dtype=torch.int32, pin_memory=True),
+                lens=torch.empty(S, dtype=torch.int32, pin_memory=True)) for _ in range(2)]
+    copied = [torch.cuda.Event(), torch.cuda.Event()]
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t_build
+
+    first = {"slots": slots0, "tables": tables0, "lens": blens}
+    lens_per_step, tables_last = [], None
+    ev = []
+
+    def step(i, timed):
+        nonlocal tables_last
+        buf = pin[i % 2]
+        copied[i % 2].synchronize()  # the copy that last read this buffer is done
+        sl, tb, ln = buf["slots"].numpy(), buf["tables"].numpy(), buf["lens"].numpy()
+        if i == 0:
+            sl[:], tb[:], ln[:] = first["slots"], first["tables"], first["lens"]
+        else:
+            rc, _ = bm.append_slots(ids, out=sl)                       # a1
+            assert rc == 0, rc
+            bm.export(ids, tables=tb, lens=ln)
+        d_slots.copy_(buf["slots"], non_blocking=True)
+        d_tables.copy_(buf["tables"], non_blocking=True)
+        d_lens.copy_(buf["lens"], non_blocking=True)
+        copied[i % 2].record(stream)
+        pkv.pkv_reshape_and_cache(w.k_new, w.v_new, w.k_cache, w.v_cache, d_slots,  # a2
+                                  w.k_scale, w.v_scale)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        pkv.pkv_decode_attention_partitions(params, out, w.q, w.k_cache, w.v_cache, d_tables,
+                                            d_lens, ws, lse)                     # a3-a6, a8
+        if timed:
+            e1.record(stream)
+            ev.append((e0, e1))
+            lens_per_step.append(ln.copy())
+            tables_last = tb
+        pkv.pkv_decode_attention_merge(params, out, d_lens, ws, lse)             # a7
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total_steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    pass1_ms = [a.elapsed_time(b) for a, b in ev]
+    pass1_avg_ms = float(np.mean(pass1_ms))
+
+    # algorithmic bytes, step by step (contexts grow by one token per step)
+    _, tables_now, _ = bm.export(ids)
+    kv_u, kv_l, oth = [], [], []
+    for ln in lens_per_step:
+        u, l = kv_bytes(spec, tables_now, ln)
+        kv_u.append(u)
+        kv_l.append(l)
+        oth.append(other_bytes(spec, ln))
+    kv_step = float(np.mean(kv_u))
+    pass1_bytes = float(np.mean(np.array(kv_u) + np.array(oth)))
+    achieved = pass1_bytes / (pass1_avg_ms * 1e-3) / 1e9
+    value = kv_step / (ms_per_step * 1e-3) / 1e9
+    seq_tok_s = S / (ms_per_step * 1e-3)
+
+    counters = traffic_from_counters()
+    traffic = counters.get("hbm_bytes_per_launch") if counters else None
+
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {workloads.F32: "f32", workloads.BF16: "bf16",
+                  workloads.E4M3: "fp8-e4m3 kv, bf16 q/out"}[spec.cache_dtype],
+        "data": "synthetic (seeded N(0,1) values, shuffled block tables)",
+        "config": {"workload": spec.name, "seqs": S, "q_heads": spec.num_q_heads,
+                   "kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim, "block_size": BS,
+                   "partition_tokens": pkv.pkv_decode_partition_size(params),
+                   "mean_context": float(np.mean(lens_per_step[0])), "parallelism": "1 GPU"},
+        "seq_tokens_per_s_per_layer": round(seq_tok_s, 1),
+        "kv_bytes_per_step": int(kv_step),
+        "kv_bytes_per_step_logical": int(np.mean(kv_l)),
+        "roofline": {"bound": "hbm", "kernel": "decode_partitions_kernel (pass 1)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": int(pass1_bytes), "avg_launch_us": round(pass1_avg_ms * 1e3, 2)},
+        "setup_s": round(build_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(spec, w, bm, ids, args, pkv, torch)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(spec, w, bm, ids, args, pkv, torch):
+    """The fp64 oracle, untuned, on a bounded sample of the same workload:
+    its cache write stores each sampled sequence's decode token and its
+    attention runs over the sampled sequences.  Host copies of the sampled
+    sequences' blocks are made before the clock starts."""
+    from oracle import oracle as O
+    import workloads
+    k = min(args.cpu_seqs or CPU_SEQS[spec.index], len(ids))
+    seqs = np.arange(k)
+    _, tables, lens = bm.export(ids[:k])
+    n = [-(-int(L) // BS) for L in lens]
+    blocks = np.unique(np.concatenate([tables[i, :n[i]] for i in range(k)]))
+    remap = np.full(int(tables.max()) + 1, -1, dtype=np.int64)
+    remap[blocks] = np.arange(len(blocks))
+    t = np.full(tables.shape, -1, dtype=np.int32)
+    for i in range(k):
+        t[i, :n[i]] = remap[tables[i, :n[i]]]
+    idx = torch.from_numpy(blocks.astype(np.int64)).to(w.k_cache.device)
+
+    def host(x):
+        x = x.cpu()
+        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
+
+    kc, vc = host(w.k_cache.index_select(0, idx)), host(w.v_cache.index_select(0, idx))
+    q = np.ascontiguousarray(host(w.q[:k]))
+    kn = np.ascontiguousarray(host(w.k_new[:k]))
+    vn = np.ascontiguousarray(host(w.v_new[:k]))
+    pos = np.maximum(lens - 1, 0)  # the decode token of each sampled sequence
+    slots = np.array([t[i, pos[i] // BS] * BS + pos[i] % BS for i in range(k)], dtype=np.int64)
+    cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    O.reshape_and_cache(kn, vn, spec.q_dtype, kc, vc, spec.cache_dtype, slots, BS, w.k_scale, w.v_scale)
+    O.decode_attention(q, spec.q_dtype, kc, vc, spec.cache_dtype, t, lens, spec.num_kv_heads, BS,
+                       w.scale, w.k_scale, w.v_scale, threads=cores)
+    secs = time.perf_counter() - t0
+    per_tok = 2 * spec.num_kv_heads * spec.head_dim * workloads.ELEM_BYTES[spec.cache_dtype]
+    kvb = int(np.sum(lens)) * per_tok
+    return {"value": round(kvb / secs / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "seq_tokens_per_s_per_layer": round(k / secs, 2), "seconds": round(secs, 2),
+            "sample": f"{k} of {len(ids)} sequences of the same step (all {spec.num_q_heads} "
+                      f"query heads, {int(np.sum(lens))} tokens): cache write + fp64 attention"}
+
+
+if __name__ == "__main__":
+    main()

@@ -20,6 +20,9 @@ HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from emitting packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the online-softmax rescale works on
+    # them with VALU ops, which cannot address AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall"]
 
