@@ -192,8 +192,11 @@ typedef struct {
 } pkv_decode_params;
 
 /* Bytes of device workspace pkv_decode_attention needs for these params
- * (0 when no sequence can span more than one partition).  The workspace
- * holds per-partition fp32 partial results; it need not be initialised. */
+ * (0 only for invalid params).  The workspace holds the pass-1 work list
+ * built on the device from context_lens and, when a sequence can span more
+ * than one partition, the per-partition fp32 partial results.  It need not be
+ * initialised; it must be 256-byte aligned.  Calls that share a workspace
+ * must be ordered on one stream. */
 size_t pkv_decode_workspace_bytes(const pkv_decode_params* p);
 
 /* The partition size (tokens) the call will use for these params. */
@@ -210,7 +213,9 @@ pkv_status pkv_decode_attention(const pkv_decode_params* p, void* out, const voi
 
 /* Pass 1 alone: every (sequence, kv head, partition) attends to its
  * partition's tokens.  A sequence that fits one partition gets its final
- * out / lse here; longer ones leave fp32 partials in the workspace. */
+ * out / lse here; longer ones leave fp32 partials in the workspace.  Work is
+ * spread over the GPU by a device-built work list that resident workgroups
+ * drain (one small planning kernel precedes the attention kernel). */
 pkv_status pkv_decode_attention_partitions(const pkv_decode_params* p, void* out, const void* q,
                                            const void* k_cache, const void* v_cache,
                                            const int32_t* block_tables,

@@ -34,7 +34,9 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Compile libpkv.so.  extra_flags go to every hipcc compile (for example
+    -DPKV_DEPTH_FP8=4 to change a tuning constant); out is the library path."""
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="pkv_build_") as tmp:
         objs = []
@@ -45,7 +47,7 @@ def build(verbose: bool = False) -> str:
             subprocess.run(cmd, check=True)
 
         kobj = os.path.join(tmp, "kernels.o")
-        run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kobj])
+        run([hipcc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kobj])
         objs.append(kobj)
         cobj = os.path.join(tmp, "capi.o")
         run([hipcc, "-x", "hip", *HIP_FLAGS, "-c", os.path.join(CSRC, "capi.cpp"), "-o", cobj])
@@ -53,10 +55,10 @@ def build(verbose: bool = False) -> str:
         bobj = os.path.join(tmp, "block_manager.o")
         run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "block_manager.cpp"), "-o", bobj])
         objs.append(bobj)
-        out_tmp = LIB + ".tmp"
+        out_tmp = out + ".tmp"
         run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp])
-        os.replace(out_tmp, LIB)
-    return LIB
+        os.replace(out_tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -16,9 +16,6 @@ namespace {
 thread_local std::string g_last_error;
 
 constexpr int32_t kBlockSize = 16;
-constexpr int32_t kDefaultPartition = 512;
-constexpr int64_t kMaxGridY = 65535;
-constexpr int64_t kMaxMergeLds = 64 * 1024;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -29,23 +26,33 @@ int elem_bytes(int32_t dt) {
 }
 
 struct Layout {
-  int32_t partition = 0;  // tokens
-  int32_t max_parts = 1;
-  size_t o_off = 0, m_off = 0, l_off = 0, e_off = 0, bytes = 0;
+  int32_t part_blocks = 0;   // partition cut every part_blocks blocks (0: none)
+  int64_t max_segments = 0;  // bound on pass-1 segment slots
+  size_t o_off = 0, m_off = 0, l_off = 0, e_off = 0;
+  size_t cum_off = 0, parts_off = 0, rpair_off = 0, bytes = 0;
 };
 
+// Workspace: fp32 partial states of at most max_segments segment slots, then
+// the plan arrays.  Slots are below (partitions of all pairs) + ranges; a pair
+// has at most ceil(blocks / part_blocks) partitions (1 without partition
+// cuts), and ranges are at most kMaxRanges.
 Layout layout_of(const pkv_decode_params& p) {
   Layout L;
-  L.partition = p.partition_size > 0 ? p.partition_size : kDefaultPartition;
-  const int64_t mc = p.max_context_len > 0 ? p.max_context_len : 0;
-  L.max_parts = mc > L.partition ? (int32_t)((mc + L.partition - 1) / L.partition) : 1;
-  if (L.max_parts <= 1) return L;
-  const size_t rows = (size_t)p.num_seqs * (size_t)p.num_q_heads * (size_t)L.max_parts;
+  L.part_blocks = p.partition_size > 0 ? p.partition_size / kBlockSize : 0;
+  const int64_t max_blocks = ((int64_t)(p.max_context_len > 0 ? p.max_context_len : 0) + kBlockSize - 1) / kBlockSize;
+  const int64_t pieces = L.part_blocks > 0 ? (max_blocks + L.part_blocks - 1) / L.part_blocks : 1;
+  const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
+  const int64_t group = p.num_kv_heads > 0 ? p.num_q_heads / p.num_kv_heads : 1;
+  L.max_segments = pairs * (pieces > 1 ? pieces : 1) + pkv::kMaxRanges;
+  const size_t rows = (size_t)L.max_segments * (size_t)group;
   L.o_off = 0;
   L.m_off = round_up(rows * (size_t)p.head_dim * sizeof(float), 256);
   L.l_off = L.m_off + round_up(rows * sizeof(float), 256);
   L.e_off = L.l_off + round_up(rows * sizeof(float), 256);
-  L.bytes = L.e_off + round_up(rows * sizeof(float), 256);
+  L.cum_off = L.e_off + round_up(rows * sizeof(float), 256);
+  L.parts_off = L.cum_off + round_up(((size_t)p.num_seqs + 1) * sizeof(int32_t), 256);
+  L.rpair_off = L.parts_off + round_up(((size_t)p.num_seqs + 1) * sizeof(int32_t), 256);
+  L.bytes = L.rpair_off + round_up((size_t)pkv::kMaxRanges * sizeof(int32_t), 256);
   return L;
 }
 
@@ -75,11 +82,10 @@ pkv_status check_decode(const pkv_decode_params* p) {
     return pkv_fail(PKV_ERR_UNSUPPORTED,
                     "decode: (q, cache, out) dtypes must be (f32,f32,f32), (bf16,bf16,bf16) or (bf16,fp8,bf16)");
   const Layout L = layout_of(*p);
-  if (L.max_parts > kMaxGridY) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: too many partitions per sequence");
-  if ((int64_t)L.max_parts * (int64_t)sizeof(float) > kMaxMergeLds)
-    return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: too many partitions per sequence");
-  if ((int64_t)p->num_seqs * p->num_q_heads > INT32_MAX)
-    return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: num_seqs * num_q_heads too large");
+  const int64_t max_blocks = ((int64_t)p->max_context_len + kBlockSize - 1) / kBlockSize;
+  if ((int64_t)p->num_seqs * p->num_q_heads > INT32_MAX || L.max_segments * 3 > INT32_MAX ||
+      (int64_t)p->num_seqs * max_blocks * p->num_kv_heads > INT32_MAX)
+    return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: sequences * heads * blocks too large");
   return PKV_OK;
 }
 
@@ -104,11 +110,9 @@ pkv_status build_args(const pkv_decode_params* p, void* out, const void* q, cons
                           !aligned(block_tables, 4))) ||
         (lse_out && !aligned(lse_out, 4)))
       return pkv_fail(PKV_ERR_INVALID_ARG, "decode: q and the caches must be 16-byte aligned, other arrays element aligned");
-    if (L.bytes > 0) {
-      if (!workspace || workspace_bytes < L.bytes)
-        return pkv_fail(PKV_ERR_INVALID_ARG, "decode: workspace missing or smaller than pkv_decode_workspace_bytes()");
-      if (!aligned(workspace, 256)) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: workspace must be 256-byte aligned");
-    }
+    if (!workspace || workspace_bytes < L.bytes)
+      return pkv_fail(PKV_ERR_INVALID_ARG, "decode: workspace missing or smaller than pkv_decode_workspace_bytes()");
+    if (!aligned(workspace, 256)) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: workspace must be 256-byte aligned");
   }
   pkv::DecodeArgs& d = *a;
   d.out = out;
@@ -118,10 +122,13 @@ pkv_status build_args(const pkv_decode_params* p, void* out, const void* q, cons
   d.block_tables = block_tables;
   d.context_lens = context_lens;
   char* ws = static_cast<char*>(const_cast<void*>(workspace));
-  d.ws_o = L.bytes ? reinterpret_cast<float*>(ws + L.o_off) : nullptr;
-  d.ws_m = L.bytes ? reinterpret_cast<float*>(ws + L.m_off) : nullptr;
-  d.ws_l = L.bytes ? reinterpret_cast<float*>(ws + L.l_off) : nullptr;
-  d.ws_e = L.bytes ? reinterpret_cast<float*>(ws + L.e_off) : nullptr;
+  d.ws_o = reinterpret_cast<float*>(ws + L.o_off);
+  d.ws_m = reinterpret_cast<float*>(ws + L.m_off);
+  d.ws_l = reinterpret_cast<float*>(ws + L.l_off);
+  d.ws_e = reinterpret_cast<float*>(ws + L.e_off);
+  d.cum = reinterpret_cast<int32_t*>(ws + L.cum_off);
+  d.cum_parts = reinterpret_cast<int32_t*>(ws + L.parts_off);
+  d.range_pair = reinterpret_cast<int32_t*>(ws + L.rpair_off);
   d.lse = lse_out;
   d.num_blocks = p->num_blocks;
   d.num_seqs = p->num_seqs;
@@ -130,11 +137,19 @@ pkv_status build_args(const pkv_decode_params* p, void* out, const void* q, cons
   d.group = p->num_q_heads / p->num_kv_heads;
   d.max_blocks = p->max_blocks_per_seq;
   d.max_context_len = p->max_context_len;
-  d.part_blocks = L.partition / kBlockSize;
-  d.max_parts = L.max_parts;
+  d.part_blocks = L.part_blocks;
+  d.num_ranges = 0;
   d.score_scale_log2 = (float)((double)p->scale * (double)p->k_scale * 1.4426950408889634);
   d.v_scale = p->v_scale;
   *lay = L;
+  // ranges of pass 1 (one per resident wave); pass 2 derives the same slots
+  if (p->num_seqs > 0) {
+    hipError_t e = hipSuccess;
+    d.num_ranges = pkv::decode_ranges(p->cache_dtype, p->head_dim,
+                                      (int64_t)p->num_seqs * p->num_kv_heads * ((int64_t)p->max_context_len + kBlockSize - 1) / kBlockSize,
+                                      &e);
+    if (e != hipSuccess) return check_hip(e, "decode: querying the device");
+  }
   return PKV_OK;
 }
 
@@ -211,7 +226,7 @@ size_t pkv_decode_workspace_bytes(const pkv_decode_params* p) {
 
 int32_t pkv_decode_partition_size(const pkv_decode_params* p) {
   if (check_decode(p) != PKV_OK) return -1;
-  return layout_of(*p).partition;
+  return layout_of(*p).part_blocks * kBlockSize;
 }
 
 pkv_status pkv_decode_attention_partitions(const pkv_decode_params* p, void* out, const void* q, const void* k_cache,

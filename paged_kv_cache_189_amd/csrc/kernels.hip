@@ -31,6 +31,7 @@
 //    second kernel merges by log-sum-exp.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "pkv_launch.h"
@@ -236,43 +237,78 @@ struct Acc {
 // K/V tiles are streamed once per step: non-temporal loads (the nt bit)
 // keep them from displacing reusable lines in L2 and measured ~12% more
 // read bandwidth on MI355X for randomly placed 4-8 KiB tiles.
+// Global-memory (address space 1) views, so loads are `global_load` with a
+// scalar base, never FLAT loads (which also hold the LDS wait counter).
+typedef const __attribute__((address_space(1))) char* gchar_p;
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+
 template <int KIND, int D>
-__device__ __forceinline__ void load_tile(Frags<KIND, D>& f, const char* kt, const char* vt,
-                                          int lane, int r, int q4) {
+__device__ __forceinline__ void load_tile(Frags<KIND, D>& f, gchar_p kt, gchar_p vt, int lane, int r,
+                                          int q4) {
   using T = Tile<KIND, D>;
   using V = typename T::V;
+  const uint32_t koff = (uint32_t)lane * 16u;
+  const uint32_t voff = (uint32_t)(r * kBS + 4 * q4) * T::ES;
 #pragma unroll
   for (int j = 0; j < T::NK; ++j)
-    f.k[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kt + (j * 64 + lane) * 16));
+    f.k[j] = __builtin_nontemporal_load(reinterpret_cast<gptr<u32x4>>(kt + koff + j * 1024));
 #pragma unroll
   for (int nt = 0; nt < T::NT; ++nt)
-    f.v[nt] = __builtin_nontemporal_load(
-        reinterpret_cast<const V*>(vt + ((nt * 16 + r) * kBS + 4 * q4) * T::ES));
+    f.v[nt] = __builtin_nontemporal_load(reinterpret_cast<gptr<V>>(vt + voff + nt * 16 * kBS * T::ES));
+}
+
+// Read-only inputs of pass 1 (tables, lengths, the plan) seen through the
+// constant address space: uniform reads of them become scalar loads, which
+// count on their own wait counter and do not hold up the K/V stream.
+template <typename T>
+using cptr = const __attribute__((address_space(4))) T*;
+template <typename T>
+__device__ __forceinline__ cptr<T> as_const(const T* p) {
+  return (cptr<T>)p;
+}
+
+// A global pointer the whole wave agrees on, moved to scalar registers.
+__device__ __forceinline__ gchar_p uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<gchar_p>(((uint64_t)hi << 32) | lo);
 }
 
 // S^T[token 4*q4+i][head r] for i = 0..3.
+// Q^T fragments of one segment's query group, staged once in LDS and shared
+// by the NW waves: qf[j][lane] is the 16 bytes lane `lane` feeds to MFMA step j.
 template <int KIND, int D>
-__device__ __forceinline__ f32x4 scores(const Frags<KIND, D>& f, const u32x4 (&qf)[Tile<KIND, D>::NQ]) {
+struct QLds {
+  u32x4 qf[Tile<KIND, D>::NQ][64];
+};
+
+// S^T[token 4*q4+i][head r] for i = 0..3.
+template <int KIND, int D>
+__device__ __forceinline__ f32x4 scores(const Frags<KIND, D>& f, const QLds<KIND, D>& q, int lane) {
   using T = Tile<KIND, D>;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (KIND == kBF16) {
 #pragma unroll
     for (int j = 0; j < T::NK; ++j)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(f.k[j]), bitcast<bf16x8>(qf[j]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(f.k[j]), bitcast<bf16x8>(q.qf[j][lane]), acc, 0, 0, 0);
   } else if constexpr (KIND == kFP8) {
 #pragma unroll
     for (int j = 0; j < T::NK; ++j) {
       u32x4 lo, hi;
       fp8x16_to_bf16(f.k[j], lo, hi);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(lo), bitcast<bf16x8>(qf[2 * j]), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(hi), bitcast<bf16x8>(qf[2 * j + 1]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(lo), bitcast<bf16x8>(q.qf[2 * j][lane]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(hi), bitcast<bf16x8>(q.qf[2 * j + 1][lane]), acc, 0, 0, 0);
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < T::NK; ++j)
+    for (int j = 0; j < T::NK; ++j) {
+      const u32x4 qj = q.qf[j][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(f.k[j][e]), __uint_as_float(qf[j][e]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(f.k[j][e]), __uint_as_float(qj[e]), acc, 0, 0, 0);
+    }
   }
   return acc;
 }
@@ -383,10 +419,10 @@ struct RunState {
 // Scores, online softmax and P.V for logical block b of the sequence.
 template <int KIND, int D>
 __device__ __forceinline__ void process_block(RunState<KIND, D>& st, const Frags<KIND, D>& f,
-                                              const u32x4 (&qf)[Tile<KIND, D>::NQ], int b, int L,
-                                              float score_scale_log2, int q4) {
+                                              const QLds<KIND, D>& q, int b, int L,
+                                              float score_scale_log2, int lane, int q4) {
   using T = Tile<KIND, D>;
-  const f32x4 sc = scores<KIND, D>(f, qf);
+  const f32x4 sc = scores<KIND, D>(f, q, lane);
   const int tok0 = b * kBS + 4 * q4;
   float x[4];
   bool valid[4];
@@ -418,27 +454,28 @@ __device__ __forceinline__ void process_block(RunState<KIND, D>& st, const Frags
     accumulate_pv<KIND, D, false>(st.acc, f, wt, valid);
 }
 
-template <int KIND, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_partitions_kernel(DecodeArgs a) {
+// LDS of one workgroup: the NW wave states of the item being merged.
+// One segment, processed by one wave: logical blocks [b_begin, b_end) of
+// sequence s under kv head g.  slot < 0: the segment is the whole sequence
+// and writes the final row; otherwise it writes partial state `slot`.
+template <int KIND, int D, int S>
+__device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D>& qs, int s, int g,
+                                               int b_begin, int b_end, int slot) {
+  static_assert(S >= 2 && S <= 4, "2 to 4 register buffers");
   using T = Tile<KIND, D>;
+  constexpr int NW = 1;  // blocks of the segment are taken in order by this wave
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q4 = lane >> 4;
-  const int g = blockIdx.x % a.num_kv_heads;
-  const int s = blockIdx.x / a.num_kv_heads;
-  const int part = blockIdx.y;
 
-  int L = a.context_lens[s];
+  int L = as_const(a.context_lens)[s];
   L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
-  const int nblk = (L + kBS - 1) / kBS;
-  const int nparts = (nblk + a.part_blocks - 1) / a.part_blocks;
-  if (part >= (nparts > 0 ? nparts : 1)) return;
 
   const int G = a.group;
   const int Hq = a.num_q_heads;
 
-  // Q^T fragments of the lane's head (zero rows pad the group to 16).
-  u32x4 qf[T::NQ];
+  // Q^T fragments of the lane's head (zero rows pad the group to 16), staged in
+  // this wave's LDS slot (a wave's LDS accesses complete in order, so no
+  // barrier is needed between segments).
   {
     const int head = g * G + r;
     constexpr int QES = KIND == kF32 ? 4 : 2;
@@ -450,180 +487,506 @@ __global__ __launch_bounds__(NW * 64) void decode_partitions_kernel(DecodeArgs a
         off = ((j >> 1) * 4 + q4) * 32 + (j & 1) * 16;
       else
         off = (j * 4 + q4) * 16;
-      qf[j] = r < G ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0u, 0u, 0u, 0u};
+      qs.qf[j][lane] = r < G ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
-  const int b_begin = part * a.part_blocks;
-  const int b_end = min(b_begin + a.part_blocks, nblk);
-  const int32_t* tbl = a.block_tables + (int64_t)s * a.max_blocks;
+  const cptr<int32_t> tbl = as_const(a.block_tables) + (int64_t)s * a.max_blocks;
   const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)g * T::BYTES;
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)g * T::BYTES;
   const int64_t bstride = (int64_t)a.num_kv_heads * T::BYTES;
   const int64_t last_block = a.num_blocks - 1;
 
-  auto tile_of = [&](int b, const char*& kt, const char*& vt) {
+  // Tile bases are wave-uniform: keep them in scalar registers so each load
+  // is a scalar base plus the lane's 32-bit offset.
+  auto tile_of = [&](int b, gchar_p& kt, gchar_p& vt) {
     int64_t phys = __builtin_amdgcn_readfirstlane(tbl[b]);
     phys = phys < 0 ? 0 : (phys > last_block ? last_block : phys);
-    kt = kbase + phys * bstride;
-    vt = vbase + phys * bstride;
+    kt = uniform_ptr(kbase + phys * bstride);
+    vt = uniform_ptr(vbase + phys * bstride);
   };
 
-  // Ping-pong register buffers: block b+NW is loaded while block b is
-  // processed.  The prefetch index is clamped (the last block is re-read from
-  // cache) so every iteration issues the same loads and the waits stay partial.
+  // S rotating register buffers: while block b is processed, the loads of
+  // blocks b+NW .. b+(S-1)*NW are in flight.  Prefetch indices are clamped
+  // (the last block is re-read from cache) so every stage issues the same
+  // loads and the waits stay partial.
   RunState<KIND, D> st;
   st.init();
-  int b = b_begin + w;
+  int b = b_begin;
   if (b < b_end) {
-    Frags<KIND, D> fa, fb;
-    const char *kt, *vt;
-    tile_of(b, kt, vt);
-    load_tile<KIND, D>(fa, kt, vt, lane, r, q4);
-    for (;;) {
-      tile_of(min(b + NW, b_end - 1), kt, vt);
-      load_tile<KIND, D>(fb, kt, vt, lane, r, q4);
-      process_block<KIND, D>(st, fa, qf, b, L, a.score_scale_log2, q4);
-      b += NW;
-      if (b >= b_end) break;
-      tile_of(min(b + NW, b_end - 1), kt, vt);
-      load_tile<KIND, D>(fa, kt, vt, lane, r, q4);
-      process_block<KIND, D>(st, fb, qf, b, L, a.score_scale_log2, q4);
-      b += NW;
-      if (b >= b_end) break;
+    Frags<KIND, D> f0, f1, f2, f3;
+    gchar_p kt, vt;
+#define PKV_PREFETCH(BUF, AHEAD)                          \
+  tile_of(min(b + (AHEAD)*NW, b_end - 1), kt, vt);        \
+  load_tile<KIND, D>(BUF, kt, vt, lane, r, q4);
+#define PKV_STAGE(CUR, NXT)                                              \
+  PKV_PREFETCH(NXT, S - 1)                                               \
+  process_block<KIND, D>(st, CUR, qs, b, L, a.score_scale_log2, lane, q4);   \
+  b += NW;                                                               \
+  if (b >= b_end) break;
+    PKV_PREFETCH(f0, 0)
+    if constexpr (S >= 3) { PKV_PREFETCH(f1, 1) }
+    if constexpr (S >= 4) { PKV_PREFETCH(f2, 2) }
+    if constexpr (S == 2) {
+      for (;;) { PKV_STAGE(f0, f1) PKV_STAGE(f1, f0) }
+    } else if constexpr (S == 3) {
+      for (;;) { PKV_STAGE(f0, f2) PKV_STAGE(f1, f0) PKV_STAGE(f2, f1) }
+    } else {
+      for (;;) { PKV_STAGE(f0, f3) PKV_STAGE(f1, f0) PKV_STAGE(f2, f1) PKV_STAGE(f3, f2) }
     }
+#undef PKV_STAGE
+#undef PKV_PREFETCH
   }
   const float m_run = st.m;
   const float l_run = sum_across_groups(st.l);
   const float e_run = sum_across_groups(st.e);
   const f32x4* o = st.acc.o;
 
-  // ---- merge the NW wave states through LDS
-  __shared__ float sm_o[NW][D][17];
-  __shared__ float sm_m[NW][16];
-  __shared__ float sm_l[NW][16];
-  __shared__ float sm_e[NW][16];
-  if (q4 == 0) {
-    sm_m[w][r] = m_run;
-    sm_l[w][r] = l_run;
-    sm_e[w][r] = e_run;
-  }
+  // ---- lane (r, q4) holds O^T[d = nt*16 + 4*q4 + i][head r]: write it out
+  if (r >= G) return;
+  const int64_t row = (int64_t)s * Hq + g * G + r;
+  if (slot < 0) {
+    const float inv = l_run > 0.f ? a.v_scale / l_run : 0.f;
 #pragma unroll
-  for (int nt = 0; nt < T::NT; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sm_o[w][nt * 16 + 4 * q4 + i][r] = o[nt][i];
-  __syncthreads();
-
-  const bool final_row = nparts <= 1;
-  for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-    const int h = e / D, d = e % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
-    float num = 0.f, den = 0.f, ex = 0.f;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const float mk = sm_m[k][h];
-      const float c = mk == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mk - M);
-      num += c * sm_o[k][d][h];
-      den += c * sm_l[k][h];
-      ex += c * sm_e[k][h];
-    }
-    const int64_t row = (int64_t)s * Hq + g * G + h;
-    if (final_row) {
-      const float val = den > 0.f ? num / den * a.v_scale : 0.f;
-      if constexpr (KIND == kF32)
-        static_cast<float*>(a.out)[row * D + d] = val;
-      else
-        static_cast<uint16_t*>(a.out)[row * D + d] = f32_to_bf16_rne(val);
-      if (d == 0 && a.lse)
-        a.lse[row] = ex > 0.f ? (M + __builtin_amdgcn_logf(ex)) * kLn2 : -INFINITY;
-    } else {
-      const int64_t pr = row * a.max_parts + part;
-      a.ws_o[pr * D + d] = num * a.v_scale;
-      if (d == 0) {
-        a.ws_m[pr] = M;
-        a.ws_l[pr] = den;
-        a.ws_e[pr] = ex;
+    for (int nt = 0; nt < T::NT; ++nt) {
+      const int d = nt * 16 + 4 * q4;
+      if constexpr (KIND == kF32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d) = o[nt] * inv;
+      } else {
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[nt][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[nt][1] * inv) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[nt][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[nt][3] * inv) << 16);
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * D + d) = u32x2{lo, hi};
       }
     }
+    if (q4 == 0 && a.lse) a.lse[row] = e_run > 0.f ? (m_run + __builtin_amdgcn_logf(e_run)) * kLn2 : -INFINITY;
+  } else {
+    const int64_t pr = (int64_t)slot * G + r;
+#pragma unroll
+    for (int nt = 0; nt < T::NT; ++nt)
+      *reinterpret_cast<f32x4*>(a.ws_o + pr * D + nt * 16 + 4 * q4) = o[nt] * a.v_scale;
+    if (q4 == 0) {
+      a.ws_m[pr] = m_run;
+      a.ws_l[pr] = l_run;
+      a.ws_e[pr] = e_run;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- planning
+// Work division, rebuilt on the device every call from context_lens.  All
+// (kv head, sequence) pairs lie on one line, head major: pair P = g * S + s
+// holds blocks [g*T + cb[s], g*T + cb[s+1]) of it, T = blocks of one head
+// (cb = prefix sums of blocks per sequence).  The line is cut into R equal
+// ranges of blocks, one per pass-1 wave.  Segments are the pieces between
+// cut points: pair starts, range starts, and (with partitions) every
+// part_blocks blocks from a pair's start.  The segment starting at position
+// x has slot  K(x) + range_of(x),  K(x) = global index of the partition
+// holding x (cp = prefix sums of partitions per sequence; a pair without
+// partition cuts is one partition).  Every cut raises K or the range index,
+// so slots grow strictly along the line: unique, and below
+// partitions + R.  A pair inside one range and one partition is finished in
+// pass 1; the others leave one partial state per segment for pass 2.
+__device__ __forceinline__ int64_t range_start(int64_t r, int64_t total, int R) {
+  return r * total / R;
+}
+// The last range starting at or before block position x (0 <= x < total).
+__device__ __forceinline__ int range_of(int64_t x, int64_t total, int R) {
+  return (int)(((x + 1) * R + total - 1) / total) - 1;
+}
+__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int s) {
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
+  return (L + kBS - 1) / kBS;
+}
+__device__ __forceinline__ int parts_of(int nblk, int pb) {
+  return pb > 0 ? (nblk + pb - 1) / pb : (nblk > 0 ? 1 : 0);
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x == 1024);
+// returns the prefix and writes the block total to *total.
+__device__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) {
+    const int y = __shfl_up(x, k);
+    if (lane >= k) x += y;
+  }
+  if (lane == 63) wave_sums[wv] = x;
+  __syncthreads();
+  if (wv == 0) {
+    int t = lane < 16 ? wave_sums[lane] : 0;
+#pragma unroll
+    for (int k = 1; k < 16; k <<= 1) {
+      const int y = __shfl_up(t, k);
+      if (lane >= k) t += y;
+    }
+    if (lane < 16) wave_sums[lane] = t;  // inclusive wave prefix
+  }
+  __syncthreads();
+  const int base = wv > 0 ? wave_sums[wv - 1] : 0;
+  *total = wave_sums[15];
+  __syncthreads();
+  return base + x - v;
+}
+
+// cb[S+1], cp[S+1] and, for every range, its first pair (pairs = S*Hkv for
+// an empty range past the end).  One workgroup; the prefix array is searched
+// in LDS when it fits.
+constexpr int kPlanLds = 8192;
+__global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
+  __shared__ int wave_sums[16];
+  __shared__ int carry_b, carry_p;
+  __shared__ int lcb[kPlanLds];
+  const int tid = threadIdx.x;
+  const int S = a.num_seqs, H = a.num_kv_heads, R = a.num_ranges, pb = a.part_blocks;
+  const bool in_lds = S + 1 <= kPlanLds;
+  if (tid == 0) {
+    carry_b = 0;
+    carry_p = 0;
+  }
+  __syncthreads();
+  for (int c0 = 0; c0 < S; c0 += 1024) {
+    const int s = c0 + tid;
+    const int nb = s < S ? seq_blocks(a, s) : 0;
+    int tb, tp;
+    const int eb = block_exclusive_scan(nb, wave_sums, &tb);
+    const int ep = block_exclusive_scan(parts_of(nb, pb), wave_sums, &tp);
+    if (s < S) {
+      a.cum[s] = carry_b + eb;
+      a.cum_parts[s] = carry_p + ep;
+      if (in_lds) lcb[s] = carry_b + eb;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      carry_b += tb;
+      carry_p += tp;
+    }
+    __syncthreads();
+  }
+  const int T = carry_b;
+  if (tid == 0) {
+    a.cum[S] = T;
+    a.cum_parts[S] = carry_p;
+  }
+  if (in_lds && tid == 0) lcb[S] = T;
+  __syncthreads();
+  const int64_t total = (int64_t)T * H;
+  // (the fallback rereads this kernel's own global writes: volatile keeps
+  // the reads from a stale vector L1 line)
+  const volatile int* cb = in_lds ? lcb : a.cum;
+  for (int r = tid; r < R; r += 1024) {
+    const int64_t st = range_start(r, total, R);
+    int P = S * H;
+    if (st < total) {
+      const int g = (int)(st / T);
+      const int x = (int)(st - (int64_t)g * T);
+      int lo = 0, hi = S;  // largest s with cb[s] <= x (then cb[s+1] > x)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cb[mid] <= x) lo = mid; else hi = mid;
+      }
+      P = g * S + lo;
+    }
+    a.range_pair[r] = P;
+  }
+}
+
+// ---------------------------------------------------------------- pass 1
+// Persistent: every wave owns one range.  Wave w of workgroup b takes range
+// ((b mod 8) * (R / (8 NW)) + b / 8) * NW + w, so the ranges a dispatcher
+// places on one XCD (workgroups are dealt to the 8 XCDs in turn) are one
+// contiguous eighth of the line -- with 8 kv heads, one head per XCD,
+// sharing that head's prefix blocks in the XCD's L2.  Waves never wait for
+// each other: no barrier, no atomics; the plan fixes every wave's work.
+template <int KIND, int D, int NW, int S>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KIND == kF32 ? 2 : 3)))
+void decode_partitions_kernel(DecodeArgs a) {
+  __shared__ QLds<KIND, D> qs[NW];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int R = a.num_ranges;
+  const int groups = R / NW;
+  const int rg = ((blockIdx.x & 7) * (groups >> 3) + (blockIdx.x >> 3)) * NW + w;
+  const int nseq = a.num_seqs, H = a.num_kv_heads, pb = a.part_blocks;
+  const cptr<int32_t> cb = as_const(a.cum);
+  const cptr<int32_t> cp = as_const(a.cum_parts);
+  const int T = cb[nseq], PT = cp[nseq];
+  const int64_t total = (int64_t)T * H;
+  int64_t x = range_start(rg, total, R);
+  const int64_t x1 = range_start(rg + 1, total, R);
+  if (x >= x1) return;
+  int P = as_const(a.range_pair)[rg];
+  int g = P / nseq, s = P % nseq;
+  while (x < x1 && g < H) {
+    const int64_t ps = (int64_t)g * T + cb[s];
+    const int nblk = cb[s + 1] - cb[s];
+    if (ps + nblk <= x) {  // pair ends at or before x (empty pairs too): next pair
+      if (++s == nseq) {
+        s = 0;
+        ++g;
+      }
+      continue;
+    }
+    const int lo = (int)(x - ps);
+    const int pidx = pb > 0 ? lo / pb : 0;
+    int hi = pb > 0 ? (pidx + 1) * pb : nblk;
+    hi = hi < nblk ? hi : nblk;
+    hi = (int64_t)hi < x1 - ps ? hi : (int)(x1 - ps);
+    const bool whole = lo == 0 && hi == nblk;
+    const int slot = g * PT + cp[s] + pidx + rg;
+    decode_segment<KIND, D, S>(a, qs[w], s, g, lo, hi, whole ? -1 : slot);
+    x = ps + hi;
   }
 }
 
 // ---------------------------------------------------------------- pass 2
-// One workgroup per (sequence, query head) whose sequence spans more than one
-// partition: M = max m_p, Lambda = sum l_p 2^{m_p - M},
-// out = sum 2^{m_p - M} o_p / Lambda, lse = (M + log2 sum e_p 2^{m_p - M}) ln 2,
-// where l_p sums the weights as multiplied into V and e_p the fp32 weights.
+// The segments of the pair at blocks [ps, pe), the same cut points pass 1
+// uses, grouped into items: without partition cuts an item is one range
+// r_lo + i touching the pair, with them an item is one partition, split at the
+// starts of the ranges inside it.  A piece starting at a range start belongs
+// to the last range starting there (earlier ones are empty).
+struct PairSegs {
+  int64_t ps, pe, total;
+  int k0, pb, R, r_lo, items;
+  bool all_nonempty;  // every range holds a block
+  __device__ __forceinline__ bool nonempty(int r) const {
+    return all_nonempty || range_start(r + 1, total, R) > range_start(r, total, R);
+  }
+  template <typename F>
+  __device__ __forceinline__ void item(int i, F&& f) const {
+    if (pb == 0) {
+      const int r = r_lo + i;
+      if (i == 0 || nonempty(r)) f(k0 + r);
+      return;
+    }
+    const int64_t a = ps + (int64_t)i * pb;
+    const int64_t b = a + pb < pe ? a + pb : pe;
+    const int ra = range_of(a, total, R), rb = range_of(b - 1, total, R);
+    f(k0 + i + ra);
+    for (int r = ra + 1; r <= rb; ++r)
+      if (nonempty(r)) f(k0 + i + r);
+  }
+};
+
+constexpr int kMergeThreads = 256;  // 4 waves per (sequence, query head)
+constexpr int kMergeWaves = kMergeThreads / 64;
+constexpr int kMergeList = 2048;     // segments listed in LDS; more take a slower walk
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) v = fmaxf(v, __shfl_xor(v, k));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int k = 1; k < kMergeWaves; ++k) m = fmaxf(m, red[k]);
+  __syncthreads();
+  return m;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMergeWaves; ++k) t += red[k];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix of one int per thread over the merge workgroup.
+__device__ __forceinline__ int merge_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) {
+    const int y = __shfl_up(x, k);
+    if (lane >= k) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  int base = 0, t = 0;
+#pragma unroll
+  for (int k = 0; k < kMergeWaves; ++k) {
+    base += k < wv ? wsum[k] : 0;
+    t += wsum[k];
+  }
+  __syncthreads();
+  *total = t;
+  return base + x - v;
+}
+
+// One workgroup of kMergeThreads per (sequence, query head).  A sequence of
+// length 0 gets a zero row and lse = -inf; one finished in pass 1 (inside
+// one range and one partition) is skipped; otherwise the partial states of
+// its segments are merged: M = max m_p, Lambda = sum l_p 2^{m_p - M},
+// out = sum 2^{m_p - M} o_p / Lambda, lse = (M + log2 sum e_p 2^{m_p - M}) ln 2
+// (l_p sums the weights as multiplied into V, e_p the fp32 weights).
+// The segments are listed in LDS with their factors 2^{m_p - M}; the waves
+// then take every fourth entry, each lane D/64 output dimensions, and the
+// four partial sums are added in LDS.
 template <int OUT, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
-  extern __shared__ float sm_c[];  // max_parts weights
-  __shared__ float sm_red[D / 64];
-  __shared__ float sm_ex[D / 64];
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int V = D / 64;
+  __shared__ int lslot[kMergeList];
+  __shared__ float lcoef[kMergeList];
+  __shared__ float red[kMergeWaves];
+  __shared__ int wsum[kMergeWaves];
+  __shared__ float psum[kMergeWaves][D];
   const int row = blockIdx.x;  // s * Hq + h
-  const int s = row / a.num_q_heads;
-  const int tid = threadIdx.x;
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.max_context_len ? a.max_context_len : L);
-  const int nblk = (L + kBS - 1) / kBS;
-  int np = (nblk + a.part_blocks - 1) / a.part_blocks;
-  if (np <= 1) return;
-  np = np < a.max_parts ? np : a.max_parts;
-  const float* mrow = a.ws_m + (int64_t)row * a.max_parts;
-  const float* lrow = a.ws_l + (int64_t)row * a.max_parts;
-  const float* erow = a.ws_e + (int64_t)row * a.max_parts;
-
+  const int S = a.num_seqs, H = a.num_kv_heads, R = a.num_ranges, pb = a.part_blocks;
+  const int s = row / a.num_q_heads, h = row % a.num_q_heads;
+  const int G = a.group;
+  const int g = h / G, hh = h % G;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const cptr<int32_t> cb = as_const(a.cum);
+  const cptr<int32_t> cp = as_const(a.cum_parts);
+  const int T = cb[S], PT = cp[S];
+  const int nblk = cb[s + 1] - cb[s];
+  if (nblk == 0) {
+    if (tid < D) {
+      if constexpr (OUT == kF32)
+        static_cast<float*>(a.out)[(int64_t)row * D + tid] = 0.f;
+      else
+        static_cast<uint16_t*>(a.out)[(int64_t)row * D + tid] = 0;
+    }
+    if (tid == 0 && a.lse) a.lse[row] = -INFINITY;
+    return;
+  }
+  PairSegs ps;
+  ps.total = (int64_t)T * H;
+  ps.ps = (int64_t)g * T + cb[s];
+  ps.pe = ps.ps + nblk;
+  ps.k0 = g * PT + cp[s];
+  ps.pb = pb;
+  ps.R = R;
+  ps.r_lo = range_of(ps.ps, ps.total, R);
+  const int r_hi = range_of(ps.pe - 1, ps.total, R);
+  if (ps.r_lo == r_hi && (pb == 0 || nblk <= pb)) return;  // finished in pass 1
+  ps.items = pb > 0 ? (nblk + pb - 1) / pb : r_hi - ps.r_lo + 1;
+  ps.all_nonempty = ps.total >= R;
+  const float* wm = a.ws_m;
+  int cnt = 0;
   float mx = -INFINITY;
-  for (int p = tid; p < np; p += D) mx = fmaxf(mx, mrow[p]);
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) mx = fmaxf(mx, __shfl_xor(mx, k));
-  if ((tid & 63) == 0) sm_red[tid >> 6] = mx;
-  __syncthreads();
-  float M = sm_red[0];
-#pragma unroll
-  for (int k = 1; k < D / 64; ++k) M = fmaxf(M, sm_red[k]);
-  __syncthreads();
-
+  for (int i = tid; i < ps.items; i += kMergeThreads)
+    ps.item(i, [&](int slot) {
+      ++cnt;
+      mx = fmaxf(mx, wm[(int64_t)slot * G + hh]);
+    });
+  const float M = block_max(mx, red);
+  int n;
+  int off = merge_scan(cnt, wsum, &n);
   float lam = 0.f, ex = 0.f;
-  for (int p = tid; p < np; p += D) {
-    const float m = mrow[p];
-    const float c = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-    sm_c[p] = c;
-    lam += c * lrow[p];
-    ex += c * erow[p];
-  }
+  float acc[V];
 #pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) {
-    lam += __shfl_xor(lam, k);
-    ex += __shfl_xor(ex, k);
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  if (n <= kMergeList) {
+    for (int i = tid; i < ps.items; i += kMergeThreads)
+      ps.item(i, [&](int slot) {
+        const int64_t pr = (int64_t)slot * G + hh;
+        const float m = wm[pr];
+        const float c = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        lam += c * a.ws_l[pr];
+        ex += c * a.ws_e[pr];
+        lslot[off] = slot;
+        lcoef[off] = c;
+        ++off;
+      });
+    __syncthreads();
+    // Four entries in flight per wave.
+    int j = wv;
+    for (; j + 3 * kMergeWaves < n; j += 4 * kMergeWaves) {
+      float x[4][V], c[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = j + u * kMergeWaves;
+        c[u] = lcoef[e];
+        const float* src = a.ws_o + ((int64_t)lslot[e] * G + hh) * D + lane * V;
+        if constexpr (V == 2) {
+          const float2 t = *reinterpret_cast<const float2*>(src);
+          x[u][0] = t.x;
+          x[u][1] = t.y;
+        } else {
+          x[u][0] = src[0];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] += c[u] != 0.f ? c[u] * x[u][v] : 0.f;
+    }
+    for (; j < n; j += kMergeWaves) {
+      const float cj = lcoef[j];
+      const float* src = a.ws_o + ((int64_t)lslot[j] * G + hh) * D + lane * V;
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] += cj != 0.f ? cj * src[v] : 0.f;
+    }
+  } else {
+    // Too many segments to list: each wave walks its share of the items.
+    for (int i = tid; i < ps.items; i += kMergeThreads)
+      ps.item(i, [&](int slot) {
+        const int64_t pr = (int64_t)slot * G + hh;
+        const float m = wm[pr];
+        const float c = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        lam += c * a.ws_l[pr];
+        ex += c * a.ws_e[pr];
+      });
+    for (int i = wv; i < ps.items; i += kMergeWaves)
+      ps.item(i, [&](int slot) {
+        const int64_t pr = (int64_t)slot * G + hh;
+        const float m = wm[pr];
+        if (m == -INFINITY) return;
+        const float c = __builtin_amdgcn_exp2f(m - M);
+        const float* src = a.ws_o + pr * D + lane * V;
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] += c * src[v];
+      });
   }
-  if ((tid & 63) == 0) {
-    sm_red[tid >> 6] = lam;
-    sm_ex[tid >> 6] = ex;
-  }
+  const float Lam = block_sum(lam, red);
+  const float Ex = block_sum(ex, red);
+#pragma unroll
+  for (int v = 0; v < V; ++v) psum[wv][lane * V + v] = acc[v];
   __syncthreads();
-  float Lam = 0.f, Ex = 0.f;
+  if (tid < D) {
+    float t = 0.f;
 #pragma unroll
-  for (int k = 0; k < D / 64; ++k) {
-    Lam += sm_red[k];
-    Ex += sm_ex[k];
+    for (int k = 0; k < kMergeWaves; ++k) t += psum[k][tid];
+    const float val = Lam > 0.f ? t / Lam : 0.f;
+    if constexpr (OUT == kF32)
+      static_cast<float*>(a.out)[(int64_t)row * D + tid] = val;
+    else
+      static_cast<uint16_t*>(a.out)[(int64_t)row * D + tid] = f32_to_bf16_rne(val);
   }
-
-  const float* orow = a.ws_o + (int64_t)row * a.max_parts * D + tid;
-  float acc0 = 0.f, acc1 = 0.f;
-  int p = 0;
-  for (; p + 1 < np; p += 2) {
-    acc0 += sm_c[p] * orow[(int64_t)p * D];
-    acc1 += sm_c[p + 1] * orow[(int64_t)(p + 1) * D];
-  }
-  if (p < np) acc0 += sm_c[p] * orow[(int64_t)p * D];
-  const float val = Lam > 0.f ? (acc0 + acc1) / Lam : 0.f;
-  if constexpr (OUT == kF32)
-    static_cast<float*>(a.out)[(int64_t)row * D + tid] = val;
-  else
-    static_cast<uint16_t*>(a.out)[(int64_t)row * D + tid] = f32_to_bf16_rne(val);
   if (tid == 0 && a.lse) a.lse[row] = Ex > 0.f ? (M + __builtin_amdgcn_logf(Ex)) * kLn2 : -INFINITY;
 }
+
+// Register buffers (prefetch depth + 1) per cache dtype.  An fp8 tile is half
+// the bytes of a bf16 tile, so it needs more tiles in flight for the same bytes.
+#ifndef PKV_DEPTH_F32
+#define PKV_DEPTH_F32 2
+#endif
+#ifndef PKV_DEPTH_BF16
+#define PKV_DEPTH_BF16 2
+#endif
+#ifndef PKV_DEPTH_FP8
+#define PKV_DEPTH_FP8 2
+#endif
+template <int KIND>
+struct Depth;
+template <>
+struct Depth<kF32> {
+  static constexpr int value = PKV_DEPTH_F32;
+};
+template <>
+struct Depth<kBF16> {
+  static constexpr int value = PKV_DEPTH_BF16;
+};
+template <>
+struct Depth<kFP8> {
+  static constexpr int value = PKV_DEPTH_FP8;
+};
 
 }  // namespace
 
@@ -648,15 +1011,73 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, int src, int cache, int D
   return hipSuccess;
 }
 
+// Workgroups of `kernel` (NW waves each) that fit on the current device at
+// once, cached per device and kernel variant.  Computed from the kernel's
+// register and LDS use against gfx950's limits (512 VGPRs per SIMD lane with
+// the accumulation registers unified, 160 KiB LDS and at most 8 waves per
+// SIMD): the runtime's occupancy query assumes 256 VGPRs here and would
+// leave two thirds of the GPU idle for a 168-register kernel.
+template <typename K>
+static int resident_groups(K kernel, int nw, hipError_t* err) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  hipFuncAttributes attr;
+  *err = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kernel));
+  if (*err != hipSuccess) return 0;
+  int cus = 0;
+  *err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (*err != hipSuccess) return 0;
+  const int regs = attr.numRegs > 0 ? (attr.numRegs + 7) / 8 * 8 : 8;
+  int waves_per_simd = 512 / regs;
+  waves_per_simd = waves_per_simd > 8 ? 8 : (waves_per_simd < 1 ? 1 : waves_per_simd);
+  int per_cu = waves_per_simd * 4 / nw;
+  const size_t lds = attr.sharedSizeBytes;
+  if (lds > 0) {
+    const int by_lds = (int)((160u * 1024u) / lds);
+    per_cu = per_cu < by_lds ? per_cu : by_lds;
+  }
+  per_cu = per_cu < 1 ? 1 : per_cu;
+  const int n = per_cu * (cus > 0 ? cus : 1);
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int decode_ranges(int cache, int D, int64_t max_blocks_total, hipError_t* err) {
+  *err = hipSuccess;
+  int groups = 0;
+#define PKV_R(C_, D_) \
+  if (cache == C_ && D == D_) groups = resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value>, kWavesPerGroup, err);
+  PKV_R(kF32, 64) PKV_R(kF32, 128) PKV_R(kBF16, 64) PKV_R(kBF16, 128) PKV_R(kFP8, 64) PKV_R(kFP8, 128)
+#undef PKV_R
+  // one range per resident wave; workgroups in multiples of 8 (one per XCD);
+  // never more ranges than the blocks that can exist
+  groups = groups / 8 * 8;
+  if (groups < 8) groups = 8;
+  const int64_t cap_groups = ((max_blocks_total + 8 * kWavesPerGroup - 1) / (8 * kWavesPerGroup)) * 8;
+  if (cap_groups < groups) groups = (int)(cap_groups < 8 ? 8 : cap_groups);
+  const int n = groups * kWavesPerGroup;
+  return n < kMaxRanges ? n : kMaxRanges / (8 * kWavesPerGroup) * (8 * kWavesPerGroup);
+}
+
 hipError_t launch_decode_partitions(const DecodeArgs& a, int cache, int D, hipStream_t stream,
                                     bool* supported) {
   *supported = true;
   if (a.num_seqs == 0) return hipSuccess;
-  dim3 grid(a.num_seqs * a.num_kv_heads, a.max_parts), block(kWavesPerGroup * 64);
-#define PKV_P1(C_, D_)                                                                          \
-  if (cache == C_ && D == D_) {                                                                 \
-    hipLaunchKernelGGL((decode_partitions_kernel<C_, D_, kWavesPerGroup>), grid, block, 0, stream, a); \
-    return hipGetLastError();                                                                   \
+  const int block = kWavesPerGroup * 64;
+#define PKV_P1(C_, D_)                                                                         \
+  if (cache == C_ && D == D_) {                                                                \
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a);                 \
+    hipError_t err = hipGetLastError();                                                        \
+    if (err != hipSuccess) return err;                                                         \
+    hipLaunchKernelGGL((decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value>),   \
+                       dim3(a.num_ranges / kWavesPerGroup), dim3(block), 0, stream, a);         \
+    return hipGetLastError();                                                                  \
   }
   PKV_P1(kF32, 64) PKV_P1(kF32, 128) PKV_P1(kBF16, 64) PKV_P1(kBF16, 128) PKV_P1(kFP8, 64)
   PKV_P1(kFP8, 128)
@@ -668,12 +1089,11 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int cache, int D, hipSt
 hipError_t launch_decode_merge(const DecodeArgs& a, int out, int D, hipStream_t stream,
                                bool* supported) {
   *supported = true;
-  if (a.num_seqs == 0 || a.max_parts <= 1) return hipSuccess;
-  dim3 grid(a.num_seqs * a.num_q_heads), block(D);
-  const size_t lds = (size_t)a.max_parts * sizeof(float);
+  if (a.num_seqs == 0) return hipSuccess;
+  dim3 grid(a.num_seqs * a.num_q_heads), block(kMergeThreads);
 #define PKV_P2(O_, D_)                                                                      \
   if (out == O_ && D == D_) {                                                               \
-    hipLaunchKernelGGL((decode_merge_kernel<O_, D_>), grid, block, lds, stream, a);         \
+    hipLaunchKernelGGL((decode_merge_kernel<O_, D_>), grid, block, 0, stream, a);           \
     return hipGetLastError();                                                               \
   }
   PKV_P2(kF32, 64) PKV_P2(kF32, 128) PKV_P2(kBF16, 64) PKV_P2(kBF16, 128)

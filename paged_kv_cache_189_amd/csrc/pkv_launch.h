@@ -17,11 +17,14 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_o;   // [S][Hq][max_parts][D]  partial sum_t e^{s_t - m} v_t (v_scale applied)
-  float* ws_m;   // [S][Hq][max_parts]     partition max, log2 units
-  float* ws_l;   // [S][Hq][max_parts]     partition sum of the weights as multiplied into V
-  float* ws_e;   // [S][Hq][max_parts]     partition sum of the fp32 weights (for lse)
+  float* ws_o;   // [segments][G][D]  partial sum_t e^{s_t - m} v_t (v_scale applied)
+  float* ws_m;   // [segments][G]     segment max, log2 units
+  float* ws_l;   // [segments][G]     sum of the weights as multiplied into V
+  float* ws_e;   // [segments][G]     sum of the fp32 weights (for lse)
   float* lse;    // [S][Hq] or null
+  int32_t* cum;         // [S + 1]  plan: prefix sums of blocks per sequence
+  int32_t* cum_parts;   // [S + 1]  plan: prefix sums of partitions per sequence
+  int32_t* range_pair;  // [R]      plan: first (kv head, sequence) pair of each range
   int64_t num_blocks;
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -29,8 +32,8 @@ struct DecodeArgs {
   int32_t group;
   int32_t max_blocks;
   int32_t max_context_len;
-  int32_t part_blocks;  // blocks per partition
-  int32_t max_parts;    // partitions of the longest allowed sequence
+  int32_t part_blocks;  // blocks per partition (0: cut only at range starts)
+  int32_t num_ranges;   // pass-1 waves, one range each (a multiple of 8 * waves per group)
   float score_scale_log2;  // scale * k_scale * log2(e)
   float v_scale;
 };
@@ -58,5 +61,11 @@ hipError_t launch_decode_merge(const DecodeArgs& a, int out_dtype, int head_dim,
 
 // Waves per workgroup of the partition kernel.
 constexpr int kWavesPerGroup = 4;
+// Upper bound of pass-1 workgroups (ranges); sizes the workspace.
+constexpr int kMaxRanges = 16384;
+
+// Pass-1 ranges (one per resident wave) for a cache dtype / head dim on the
+// current device, capped by the number of blocks that can exist.
+int decode_ranges(int cache_dtype, int head_dim, int64_t max_blocks_total, hipError_t* err);
 
 }  // namespace pkv

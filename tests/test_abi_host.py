@@ -161,15 +161,27 @@ def params(**kw):
     return p
 
 
+MAX_RANGES = 16384
+
+
+def _ws_expected(S, Hq, Hkv, D, max_ctx, part_tokens):
+    """Partial states for (partitions of all pairs + ranges) slots, then the
+    prefix sums of blocks and partitions per sequence and each range's first pair."""
+    r256 = lambda x: -(-x // 256) * 256
+    blocks = -(-max_ctx // 16)
+    pieces = -(-blocks // (part_tokens // 16)) if part_tokens else 1
+    segs = S * Hkv * max(pieces, 1) + MAX_RANGES
+    rows = segs * (Hq // Hkv)
+    return (r256(rows * D * 4) + 3 * r256(rows * 4) + 2 * r256((S + 1) * 4)
+            + r256(MAX_RANGES * 4))
+
+
 def test_workspace_and_partition_sizing():
     p = params()
-    assert pkv.pkv_decode_partition_size(p) == 512
-    parts = 2
-    rows = 2 * 8 * parts
-    want = -(-rows * 128 * 4 // 256) * 256 + 3 * (-(-rows * 4 // 256) * 256)
-    assert pkv.pkv_decode_workspace_bytes(p) == want
-    assert pkv.pkv_decode_workspace_bytes(params(max_context_len=512)) == 0
+    assert pkv.pkv_decode_partition_size(p) == 0  # balanced ranges only
+    assert pkv.pkv_decode_workspace_bytes(p) == _ws_expected(2, 8, 2, 128, 1024, 0)
     assert pkv.pkv_decode_partition_size(params(partition_size=256)) == 256
+    assert pkv.pkv_decode_workspace_bytes(params(partition_size=256)) == _ws_expected(2, 8, 2, 128, 1024, 256)
     assert pkv.pkv_decode_workspace_bytes(params(head_dim=96)) == 0  # invalid -> 0
 
 
