@@ -145,7 +145,7 @@ pkv_status build_args(const pkv_decode_params* p, void* out, const void* q, cons
   // ranges of pass 1 (one per resident wave); pass 2 derives the same slots
   if (p->num_seqs > 0) {
     hipError_t e = hipSuccess;
-    d.num_ranges = pkv::decode_ranges(p->cache_dtype, p->head_dim,
+    d.num_ranges = pkv::decode_ranges(p->cache_dtype, p->head_dim, p->num_seqs,
                                       (int64_t)p->num_seqs * p->num_kv_heads * ((int64_t)p->max_context_len + kBlockSize - 1) / kBlockSize,
                                       &e);
     if (e != hipSuccess) return check_hip(e, "decode: querying the device");

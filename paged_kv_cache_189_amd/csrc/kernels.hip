@@ -602,9 +602,10 @@ __device__ __forceinline__ int parts_of(int nblk, int pb) {
   return pb > 0 ? (nblk + pb - 1) / pb : (nblk > 0 ? 1 : 0);
 }
 
-// Block-wide exclusive scan of one int per thread (blockDim.x == 1024);
+// Block-wide exclusive scan of one int per thread (blockDim.x == 64 * NWV);
 // returns the prefix and writes the block total to *total.
-__device__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
+template <int NWV>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -615,19 +616,34 @@ __device__ int block_exclusive_scan(int v, int* wave_sums, int* total) {
   if (lane == 63) wave_sums[wv] = x;
   __syncthreads();
   if (wv == 0) {
-    int t = lane < 16 ? wave_sums[lane] : 0;
+    int t = lane < NWV ? wave_sums[lane] : 0;
 #pragma unroll
-    for (int k = 1; k < 16; k <<= 1) {
+    for (int k = 1; k < NWV; k <<= 1) {
       const int y = __shfl_up(t, k);
       if (lane >= k) t += y;
     }
-    if (lane < 16) wave_sums[lane] = t;  // inclusive wave prefix
+    if (lane < NWV) wave_sums[lane] = t;  // inclusive wave prefix
   }
   __syncthreads();
   const int base = wv > 0 ? wave_sums[wv - 1] : 0;
-  *total = wave_sums[15];
+  *total = wave_sums[NWV - 1];
   __syncthreads();
   return base + x - v;
+}
+
+// The pair holding block position st of the line (S * H past the end),
+// searched in the prefix array cb[0..S].
+template <typename CB>
+__device__ __forceinline__ int pair_at(int64_t st, int64_t total, int T, int S, int H, CB cb) {
+  if (st >= total) return S * H;
+  const int g = (int)(st / T);
+  const int x = (int)(st - (int64_t)g * T);
+  int lo = 0, hi = S;  // largest s with cb[s] <= x (then cb[s+1] > x)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cb[mid] <= x) lo = mid; else hi = mid;
+  }
+  return g * S + lo;
 }
 
 // cb[S+1], cp[S+1] and, for every range, its first pair (pairs = S*Hkv for
@@ -650,8 +666,8 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
     const int s = c0 + tid;
     const int nb = s < S ? seq_blocks(a, s) : 0;
     int tb, tp;
-    const int eb = block_exclusive_scan(nb, wave_sums, &tb);
-    const int ep = block_exclusive_scan(parts_of(nb, pb), wave_sums, &tp);
+    const int eb = block_exclusive_scan<16>(nb, wave_sums, &tb);
+    const int ep = block_exclusive_scan<16>(parts_of(nb, pb), wave_sums, &tp);
     if (s < S) {
       a.cum[s] = carry_b + eb;
       a.cum_parts[s] = carry_p + ep;
@@ -675,21 +691,8 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
   // (the fallback rereads this kernel's own global writes: volatile keeps
   // the reads from a stale vector L1 line)
   const volatile int* cb = in_lds ? lcb : a.cum;
-  for (int r = tid; r < R; r += 1024) {
-    const int64_t st = range_start(r, total, R);
-    int P = S * H;
-    if (st < total) {
-      const int g = (int)(st / T);
-      const int x = (int)(st - (int64_t)g * T);
-      int lo = 0, hi = S;  // largest s with cb[s] <= x (then cb[s+1] > x)
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (cb[mid] <= x) lo = mid; else hi = mid;
-      }
-      P = g * S + lo;
-    }
-    a.range_pair[r] = P;
-  }
+  for (int r = tid; r < R; r += 1024)
+    a.range_pair[r] = pair_at(range_start(r, total, R), total, T, S, H, cb);
 }
 
 // ---------------------------------------------------------------- pass 1
@@ -698,28 +701,73 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
 // places on one XCD (workgroups are dealt to the 8 XCDs in turn) are one
 // contiguous eighth of the line -- with 8 kv heads, one head per XCD,
 // sharing that head's prefix blocks in the XCD's L2.  Waves never wait for
-// each other: no barrier, no atomics; the plan fixes every wave's work.
-template <int KIND, int D, int NW, int S>
+// each other: no atomics, and the only barriers are those of the plan.
+// PLAN (up to kFusedPlanSeqs sequences): every workgroup builds the prefix
+// arrays in its LDS from context_lens and each wave finds its first pair;
+// workgroup 0 also stores them for pass 2.  Otherwise decode_plan_kernel
+// has built them beforehand.
+constexpr int kFusedPlanSeqs = 1024;
+template <int KIND, int D, int NW, int S, bool PLAN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KIND == kF32 ? 2 : 3)))
 void decode_partitions_kernel(DecodeArgs a) {
   __shared__ QLds<KIND, D> qs[NW];
+  __shared__ int lcb[PLAN ? kFusedPlanSeqs + 1 : 1];
+  __shared__ int lcp[PLAN ? kFusedPlanSeqs + 1 : 1];
+  __shared__ int wsums[NW];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int R = a.num_ranges;
   const int groups = R / NW;
   const int rg = ((blockIdx.x & 7) * (groups >> 3) + (blockIdx.x >> 3)) * NW + w;
   const int nseq = a.num_seqs, H = a.num_kv_heads, pb = a.part_blocks;
-  const cptr<int32_t> cb = as_const(a.cum);
-  const cptr<int32_t> cp = as_const(a.cum_parts);
-  const int T = cb[nseq], PT = cp[nseq];
+  if constexpr (PLAN) {
+    const int tid = threadIdx.x;
+    int carry_b = 0, carry_p = 0;
+    for (int c0 = 0; c0 < nseq; c0 += NW * 64) {
+      const int s = c0 + tid;
+      const int nb = s < nseq ? seq_blocks(a, s) : 0;
+      int tb, tp;
+      const int eb = block_exclusive_scan<NW>(nb, wsums, &tb);
+      const int ep = block_exclusive_scan<NW>(parts_of(nb, pb), wsums, &tp);
+      if (s < nseq) {
+        lcb[s] = carry_b + eb;
+        lcp[s] = carry_p + ep;
+      }
+      carry_b += tb;
+      carry_p += tp;
+    }
+    if (tid == 0) {
+      lcb[nseq] = carry_b;
+      lcp[nseq] = carry_p;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int s = tid; s <= nseq; s += NW * 64) {
+        a.cum[s] = lcb[s];
+        a.cum_parts[s] = lcp[s];
+      }
+  }
+  const cptr<int32_t> gcb = as_const(a.cum);
+  const cptr<int32_t> gcp = as_const(a.cum_parts);
+  auto cb = [&](int i) -> int {
+    if constexpr (PLAN) return lcb[i]; else return gcb[i];
+  };
+  auto cp = [&](int i) -> int {
+    if constexpr (PLAN) return lcp[i]; else return gcp[i];
+  };
+  const int T = cb(nseq), PT = cp(nseq);
   const int64_t total = (int64_t)T * H;
   int64_t x = range_start(rg, total, R);
   const int64_t x1 = range_start(rg + 1, total, R);
   if (x >= x1) return;
-  int P = as_const(a.range_pair)[rg];
+  int P;
+  if constexpr (PLAN)
+    P = pair_at(x, total, T, nseq, H, lcb);
+  else
+    P = as_const(a.range_pair)[rg];
   int g = P / nseq, s = P % nseq;
   while (x < x1 && g < H) {
-    const int64_t ps = (int64_t)g * T + cb[s];
-    const int nblk = cb[s + 1] - cb[s];
+    const int64_t ps = (int64_t)g * T + cb(s);
+    const int nblk = cb(s + 1) - cb(s);
     if (ps + nblk <= x) {  // pair ends at or before x (empty pairs too): next pair
       if (++s == nseq) {
         s = 0;
@@ -733,7 +781,7 @@ void decode_partitions_kernel(DecodeArgs a) {
     hi = hi < nblk ? hi : nblk;
     hi = (int64_t)hi < x1 - ps ? hi : (int)(x1 - ps);
     const bool whole = lo == 0 && hi == nblk;
-    const int slot = g * PT + cp[s] + pidx + rg;
+    const int slot = g * PT + cp(s) + pidx + rg;
     decode_segment<KIND, D, S>(a, qs[w], s, g, lo, hi, whole ? -1 : slot);
     x = ps + hi;
   }
@@ -796,28 +844,6 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-// Exclusive prefix of one int per thread over the merge workgroup.
-__device__ __forceinline__ int merge_scan(int v, int* wsum, int* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int k = 1; k < 64; k <<= 1) {
-    const int y = __shfl_up(x, k);
-    if (lane >= k) x += y;
-  }
-  if (lane == 63) wsum[wv] = x;
-  __syncthreads();
-  int base = 0, t = 0;
-#pragma unroll
-  for (int k = 0; k < kMergeWaves; ++k) {
-    base += k < wv ? wsum[k] : 0;
-    t += wsum[k];
-  }
-  __syncthreads();
-  *total = t;
-  return base + x - v;
-}
-
 // One workgroup of kMergeThreads per (sequence, query head).  A sequence of
 // length 0 gets a zero row and lse = -inf; one finished in pass 1 (inside
 // one range and one partition) is skipped; otherwise the partial states of
@@ -877,7 +903,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
     });
   const float M = block_max(mx, red);
   int n;
-  int off = merge_scan(cnt, wsum, &n);
+  int off = block_exclusive_scan<kMergeWaves>(cnt, wsum, &n);
   float lam = 0.f, ex = 0.f;
   float acc[V];
 #pragma unroll
@@ -1048,11 +1074,14 @@ static int resident_groups(K kernel, int nw, hipError_t* err) {
   return n;
 }
 
-int decode_ranges(int cache, int D, int64_t max_blocks_total, hipError_t* err) {
+int decode_ranges(int cache, int D, int num_seqs, int64_t max_blocks_total, hipError_t* err) {
   *err = hipSuccess;
   int groups = 0;
-#define PKV_R(C_, D_) \
-  if (cache == C_ && D == D_) groups = resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value>, kWavesPerGroup, err);
+  const bool plan = num_seqs <= kFusedPlanSeqs;
+#define PKV_R(C_, D_)                                                                              \
+  if (cache == C_ && D == D_)                                                                      \
+    groups = plan ? resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, true>, kWavesPerGroup, err) \
+                  : resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, false>, kWavesPerGroup, err);
   PKV_R(kF32, 64) PKV_R(kF32, 128) PKV_R(kBF16, 64) PKV_R(kBF16, 128) PKV_R(kFP8, 64) PKV_R(kFP8, 128)
 #undef PKV_R
   // one range per resident wave; workgroups in multiples of 8 (one per XCD);
@@ -1070,14 +1099,20 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int cache, int D, hipSt
   *supported = true;
   if (a.num_seqs == 0) return hipSuccess;
   const int block = kWavesPerGroup * 64;
-#define PKV_P1(C_, D_)                                                                         \
-  if (cache == C_ && D == D_) {                                                                \
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a);                 \
-    hipError_t err = hipGetLastError();                                                        \
-    if (err != hipSuccess) return err;                                                         \
-    hipLaunchKernelGGL((decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value>),   \
-                       dim3(a.num_ranges / kWavesPerGroup), dim3(block), 0, stream, a);         \
-    return hipGetLastError();                                                                  \
+  const dim3 grid(a.num_ranges / kWavesPerGroup);
+#define PKV_P1(C_, D_)                                                                          \
+  if (cache == C_ && D == D_) {                                                                 \
+    if (a.num_seqs <= kFusedPlanSeqs) {                                                         \
+      hipLaunchKernelGGL((decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, true>), \
+                         grid, dim3(block), 0, stream, a);                                      \
+      return hipGetLastError();                                                                 \
+    }                                                                                           \
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a);                  \
+    hipError_t err = hipGetLastError();                                                         \
+    if (err != hipSuccess) return err;                                                          \
+    hipLaunchKernelGGL((decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, false>), \
+                       grid, dim3(block), 0, stream, a);                                        \
+    return hipGetLastError();                                                                   \
   }
   PKV_P1(kF32, 64) PKV_P1(kF32, 128) PKV_P1(kBF16, 64) PKV_P1(kBF16, 128) PKV_P1(kFP8, 64)
   PKV_P1(kFP8, 128)

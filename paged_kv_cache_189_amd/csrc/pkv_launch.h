@@ -64,8 +64,9 @@ constexpr int kWavesPerGroup = 4;
 // Upper bound of pass-1 workgroups (ranges); sizes the workspace.
 constexpr int kMaxRanges = 16384;
 
-// Pass-1 ranges (one per resident wave) for a cache dtype / head dim on the
-// current device, capped by the number of blocks that can exist.
-int decode_ranges(int cache_dtype, int head_dim, int64_t max_blocks_total, hipError_t* err);
+// Pass-1 ranges (one per resident wave) for a cache dtype / head dim / batch
+// size on the current device, capped by the number of blocks that can exist.
+int decode_ranges(int cache_dtype, int head_dim, int num_seqs, int64_t max_blocks_total,
+                  hipError_t* err);
 
 }  // namespace pkv
