@@ -454,13 +454,29 @@ __device__ __forceinline__ void process_block(RunState<KIND, D>& st, const Frags
     accumulate_pv<KIND, D, false>(st.acc, f, wt, valid);
 }
 
-// LDS of one workgroup: the NW wave states of the item being merged.
+// A SIMD issues for its oldest wave first, so waves given equal work finish
+// in the order they started, the youngest far behind.  Each wave lowers its
+// own priority as it gets through its work (`done` of `total` blocks, in
+// four steps), which lets the waves that are behind catch up.
+__device__ __forceinline__ void pace(int done, int total) {
+  if (done * 4 < total)
+    __builtin_amdgcn_s_setprio(3);
+  else if (done * 2 < total)
+    __builtin_amdgcn_s_setprio(2);
+  else if (done * 4 < 3 * total)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // One segment, processed by one wave: logical blocks [b_begin, b_end) of
 // sequence s under kv head g.  slot < 0: the segment is the whole sequence
 // and writes the final row; otherwise it writes partial state `slot`.
+// done / total: the wave's progress through its range before this segment.
 template <int KIND, int D, int S>
 __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D>& qs, int s, int g,
-                                               int b_begin, int b_end, int slot) {
+                                               int b_begin, int b_end, int slot, int done,
+                                               int total) {
   static_assert(S >= 2 && S <= 4, "2 to 4 register buffers");
   using T = Tile<KIND, D>;
   constexpr int NW = 1;  // blocks of the segment are taken in order by this wave
@@ -473,13 +489,15 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
   const int G = a.group;
   const int Hq = a.num_q_heads;
 
-  // Q^T fragments of the lane's head (zero rows pad the group to 16), staged in
-  // this wave's LDS slot (a wave's LDS accesses complete in order, so no
-  // barrier is needed between segments).
+  // Q^T fragments of the lane's head (zero rows pad the group to 16).  They
+  // are loaded first and written to this wave's LDS slot once the first K/V
+  // tiles are on their way, so the three latencies (Q, table, tile) overlap.
+  // A wave's LDS accesses complete in order: no barrier between segments.
+  u32x4 qreg[T::NQ];
   {
     const int head = g * G + r;
     constexpr int QES = KIND == kF32 ? 4 : 2;
-    const char* qrow = static_cast<const char*>(a.q) + ((int64_t)s * Hq + head) * D * QES;
+    const gchar_p qrow = (gchar_p) static_cast<const char*>(a.q) + ((int64_t)s * Hq + head) * D * QES;
 #pragma unroll
     for (int j = 0; j < T::NQ; ++j) {
       int off;
@@ -487,7 +505,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
         off = ((j >> 1) * 4 + q4) * 32 + (j & 1) * 16;
       else
         off = (j * 4 + q4) * 16;
-      qs.qf[j][lane] = r < G ? *reinterpret_cast<const u32x4*>(qrow + off) : u32x4{0u, 0u, 0u, 0u};
+      qreg[j] = r < G ? *reinterpret_cast<gptr<u32x4>>(qrow + off) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -522,11 +540,14 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
 #define PKV_STAGE(CUR, NXT)                                              \
   PKV_PREFETCH(NXT, S - 1)                                               \
   process_block<KIND, D>(st, CUR, qs, b, L, a.score_scale_log2, lane, q4);   \
+  pace(done + (b - b_begin), total);                                     \
   b += NW;                                                               \
   if (b >= b_end) break;
     PKV_PREFETCH(f0, 0)
     if constexpr (S >= 3) { PKV_PREFETCH(f1, 1) }
     if constexpr (S >= 4) { PKV_PREFETCH(f2, 2) }
+#pragma unroll
+    for (int j = 0; j < T::NQ; ++j) qs.qf[j][lane] = qreg[j];
     if constexpr (S == 2) {
       for (;;) { PKV_STAGE(f0, f1) PKV_STAGE(f1, f0) }
     } else if constexpr (S == 3) {
@@ -759,6 +780,7 @@ void decode_partitions_kernel(DecodeArgs a) {
   int64_t x = range_start(rg, total, R);
   const int64_t x1 = range_start(rg + 1, total, R);
   if (x >= x1) return;
+  const int64_t x_first = x;
   int P;
   if constexpr (PLAN)
     P = pair_at(x, total, T, nseq, H, lcb);
@@ -782,7 +804,8 @@ void decode_partitions_kernel(DecodeArgs a) {
     hi = (int64_t)hi < x1 - ps ? hi : (int)(x1 - ps);
     const bool whole = lo == 0 && hi == nblk;
     const int slot = g * PT + cp(s) + pidx + rg;
-    decode_segment<KIND, D, S>(a, qs[w], s, g, lo, hi, whole ? -1 : slot);
+    decode_segment<KIND, D, S>(a, qs[w], s, g, lo, hi, whole ? -1 : slot, (int)(x - x_first),
+                               (int)(x1 - x_first));
     x = ps + hi;
   }
 }
