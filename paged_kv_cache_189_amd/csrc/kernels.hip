@@ -469,14 +469,27 @@ __device__ __forceinline__ void pace(int done, int total) {
     __builtin_amdgcn_s_setprio(0);
 }
 
+// A wave's un-reduced online-softmax state (per lane), handed to the wave
+// of the previous range through LDS.
+template <int KIND, int D>
+struct FoldLds {
+  f32x4 o[Tile<KIND, D>::NT][64];
+  float m[64], l[64], e[64];
+};
+
 // One segment, processed by one wave: logical blocks [b_begin, b_end) of
 // sequence s under kv head g.  slot < 0: the segment is the whole sequence
 // and writes the final row; otherwise it writes partial state `slot`.
 // done / total: the wave's progress through its range before this segment.
+// absorb >= 0: before writing, wait for the state published in fold[absorb]
+// (the same pair's piece in the next range) and merge it in.  publish >= 0:
+// instead of writing, hand the state to the previous range's wave through
+// fold[publish] and raise flag[publish].
 template <int KIND, int D, int S>
-__device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D>& qs, int s, int g,
+__device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D>& qs,
+                                               FoldLds<KIND, D>* fold, int* flag, int s, int g,
                                                int b_begin, int b_end, int slot, int done,
-                                               int total) {
+                                               int total, int absorb, int publish) {
   static_assert(S >= 2 && S <= 4, "2 to 4 register buffers");
   using T = Tile<KIND, D>;
   constexpr int NW = 1;  // blocks of the segment are taken in order by this wave
@@ -558,6 +571,35 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
 #undef PKV_STAGE
 #undef PKV_PREFETCH
   }
+  if (absorb >= 0) {
+    // The publisher finishes its piece before or, when that piece is its
+    // whole range, about when this wave does; the bound only guards against
+    // a hang.
+    for (int spin = 0; spin < (1 << 24); ++spin) {
+      if (__hip_atomic_load(&flag[absorb], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    const FoldLds<KIND, D>& f = fold[absorb];
+    const float mb = f.m[lane];
+    const float M = fmaxf(st.m, mb);
+    const float ca = st.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m - M);
+    const float cb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb - M);
+    st.m = M;
+    st.l = ca * st.l + cb * f.l[lane];
+    st.e = ca * st.e + cb * f.e[lane];
+#pragma unroll
+    for (int nt = 0; nt < T::NT; ++nt) st.acc.o[nt] = ca * st.acc.o[nt] + cb * f.o[nt][lane];
+  }
+  if (publish >= 0) {
+    FoldLds<KIND, D>& f = fold[publish];
+#pragma unroll
+    for (int nt = 0; nt < T::NT; ++nt) f.o[nt][lane] = st.acc.o[nt];
+    f.m[lane] = st.m;
+    f.l[lane] = st.l;
+    f.e[lane] = st.e;
+    __hip_atomic_store(&flag[publish], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return;
+  }
   const float m_run = st.m;
   const float l_run = sum_across_groups(st.l);
   const float e_run = sum_across_groups(st.e);
@@ -584,7 +626,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
     const int64_t pr = (int64_t)slot * G + r;
 #pragma unroll
     for (int nt = 0; nt < T::NT; ++nt)
-      *reinterpret_cast<f32x4*>(a.ws_o + pr * D + nt * 16 + 4 * q4) = o[nt] * a.v_scale;
+      __builtin_nontemporal_store(o[nt] * a.v_scale, reinterpret_cast<f32x4*>(a.ws_o + pr * D + nt * 16 + 4 * q4));
     if (q4 == 0) {
       a.ws_m[pr] = m_run;
       a.ws_l[pr] = l_run;
@@ -721,17 +763,20 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
 // ((b mod 8) * (R / (8 NW)) + b / 8) * NW + w, so the ranges a dispatcher
 // places on one XCD (workgroups are dealt to the 8 XCDs in turn) are one
 // contiguous eighth of the line -- with 8 kv heads, one head per XCD,
-// sharing that head's prefix blocks in the XCD's L2.  Waves never wait for
-// each other: no atomics, and the only barriers are those of the plan.
+// sharing that head's prefix blocks in the XCD's L2.  No atomics and no
+// barrier beyond the plan's; a wave waits only for the next wave of its
+// workgroup, when their ranges share a pair (folding, below).
 // PLAN (up to kFusedPlanSeqs sequences): every workgroup builds the prefix
 // arrays in its LDS from context_lens and each wave finds its first pair;
 // workgroup 0 also stores them for pass 2.  Otherwise decode_plan_kernel
 // has built them beforehand.
 constexpr int kFusedPlanSeqs = 1024;
 template <int KIND, int D, int NW, int S, bool PLAN>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(KIND == kF32 ? 2 : 3)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partitions_kernel(DecodeArgs a) {
   __shared__ QLds<KIND, D> qs[NW];
+  __shared__ FoldLds<KIND, D> fold[NW - 1];
+  __shared__ int flag[NW - 1];
   __shared__ int lcb[PLAN ? kFusedPlanSeqs + 1 : 1];
   __shared__ int lcp[PLAN ? kFusedPlanSeqs + 1 : 1];
   __shared__ int wsums[NW];
@@ -740,6 +785,8 @@ void decode_partitions_kernel(DecodeArgs a) {
   const int groups = R / NW;
   const int rg = ((blockIdx.x & 7) * (groups >> 3) + (blockIdx.x >> 3)) * NW + w;
   const int nseq = a.num_seqs, H = a.num_kv_heads, pb = a.part_blocks;
+  if (threadIdx.x < NW - 1) flag[threadIdx.x] = 0;
+  if constexpr (!PLAN) __syncthreads();
   if constexpr (PLAN) {
     const int tid = threadIdx.x;
     int carry_b = 0, carry_p = 0;
@@ -781,6 +828,8 @@ void decode_partitions_kernel(DecodeArgs a) {
   const int64_t x1 = range_start(rg + 1, total, R);
   if (x >= x1) return;
   const int64_t x_first = x;
+  // Folding needs every range non-empty and no partition cuts.
+  const bool fold_on = pb == 0 && total >= R;
   int P;
   if constexpr (PLAN)
     P = pair_at(x, total, T, nseq, H, lcb);
@@ -802,10 +851,21 @@ void decode_partitions_kernel(DecodeArgs a) {
     int hi = pb > 0 ? (pidx + 1) * pb : nblk;
     hi = hi < nblk ? hi : nblk;
     hi = (int64_t)hi < x1 - ps ? hi : (int)(x1 - ps);
-    const bool whole = lo == 0 && hi == nblk;
+    // Folding: a pair's pieces in the ranges of one workgroup are merged in
+    // LDS into the leftmost one, which alone writes (the final row when the
+    // pair starts there and ends in this workgroup).  A wave publishes its
+    // first piece when the pair began in an earlier range; before writing
+    // (or publishing) a last piece whose pair goes on into the next range of
+    // the workgroup, it absorbs that range's first piece.  Waits only ever
+    // point to the next wave, so they end.
+    const int64_t pe = ps + nblk;
+    const bool publish = fold_on && x == x_first && lo > 0 && w != 0;
+    const bool absorb = fold_on && ps + hi == x1 && hi < nblk && w != NW - 1;
+    const bool whole = fold_on ? lo == 0 && range_of(pe - 1, total, R) / NW == rg / NW : lo == 0 && hi == nblk;
     const int slot = g * PT + cp(s) + pidx + rg;
-    decode_segment<KIND, D, S>(a, qs[w], s, g, lo, hi, whole ? -1 : slot, (int)(x - x_first),
-                               (int)(x1 - x_first));
+    decode_segment<KIND, D, S>(a, qs[w], fold, flag, s, g, lo, hi, whole ? -1 : slot,
+                               (int)(x - x_first), (int)(x1 - x_first), absorb ? w : -1,
+                               publish ? w - 1 : -1);
     x = ps + hi;
   }
 }
@@ -815,19 +875,25 @@ void decode_partitions_kernel(DecodeArgs a) {
 // uses, grouped into items: without partition cuts an item is one range
 // r_lo + i touching the pair, with them an item is one partition, split at the
 // starts of the ranges inside it.  A piece starting at a range start belongs
-// to the last range starting there (earlier ones are empty).
+// to the last range starting there (earlier ones are empty).  With folding
+// (no partition cuts, every range non-empty) a piece starting at range r's
+// start, r not first in its workgroup, was merged by pass 1 into range
+// r - 1's piece and holds no state of its own.
 struct PairSegs {
   int64_t ps, pe, total;
   int k0, pb, R, r_lo, items;
   bool all_nonempty;  // every range holds a block
+  bool fold;
   __device__ __forceinline__ bool nonempty(int r) const {
     return all_nonempty || range_start(r + 1, total, R) > range_start(r, total, R);
   }
+  // (r > r_lo) the piece starting at range r's start was folded
+  __device__ __forceinline__ bool folded(int r) const { return r % kWavesPerGroup != 0; }
   template <typename F>
   __device__ __forceinline__ void item(int i, F&& f) const {
     if (pb == 0) {
       const int r = r_lo + i;
-      if (i == 0 || nonempty(r)) f(k0 + r);
+      if (i == 0 || (fold ? !folded(r) : nonempty(r))) f(k0 + r);
       return;
     }
     const int64_t a = ps + (int64_t)i * pb;
@@ -913,9 +979,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   ps.R = R;
   ps.r_lo = range_of(ps.ps, ps.total, R);
   const int r_hi = range_of(ps.pe - 1, ps.total, R);
-  if (ps.r_lo == r_hi && (pb == 0 || nblk <= pb)) return;  // finished in pass 1
-  ps.items = pb > 0 ? (nblk + pb - 1) / pb : r_hi - ps.r_lo + 1;
   ps.all_nonempty = ps.total >= R;
+  ps.fold = pb == 0 && ps.all_nonempty;
+  // finished in pass 1
+  if (ps.r_lo == r_hi && (pb == 0 || nblk <= pb)) return;
+  if (ps.fold && ps.r_lo / kWavesPerGroup == r_hi / kWavesPerGroup) return;
+  ps.items = pb > 0 ? (nblk + pb - 1) / pb : r_hi - ps.r_lo + 1;
   const float* wm = a.ws_m;
   int cnt = 0;
   float mx = -INFINITY;
@@ -1011,16 +1080,17 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   if (tid == 0 && a.lse) a.lse[row] = Ex > 0.f ? (M + __builtin_amdgcn_logf(Ex)) * kLn2 : -INFINITY;
 }
 
-// Register buffers (prefetch depth + 1) per cache dtype.  An fp8 tile is half
-// the bytes of a bf16 tile, so it needs more tiles in flight for the same bytes.
+// Register buffers (prefetch depth + 1) per cache dtype, at two waves per
+// SIMD (eight per CU).  Three measured the same as two buffers at three
+// waves per SIMD, and leave registers for the fold merge.
 #ifndef PKV_DEPTH_F32
 #define PKV_DEPTH_F32 2
 #endif
 #ifndef PKV_DEPTH_BF16
-#define PKV_DEPTH_BF16 2
+#define PKV_DEPTH_BF16 3
 #endif
 #ifndef PKV_DEPTH_FP8
-#define PKV_DEPTH_FP8 2
+#define PKV_DEPTH_FP8 3
 #endif
 template <int KIND>
 struct Depth;
@@ -1061,19 +1131,20 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, int src, int cache, int D
 }
 
 // Workgroups of `kernel` (NW waves each) that fit on the current device at
-// once, cached per device and kernel variant.  Computed from the kernel's
+// once, cached per device and kernel variant (`variant` < 16 names it).  Computed from the kernel's
 // register and LDS use against gfx950's limits (512 VGPRs per SIMD lane with
 // the accumulation registers unified, 160 KiB LDS and at most 8 waves per
 // SIMD): the runtime's occupancy query assumes 256 VGPRs here and would
 // leave two thirds of the GPU idle for a 168-register kernel.
 template <typename K>
-static int resident_groups(K kernel, int nw, hipError_t* err) {
-  static std::atomic<int> cache[64];
+static int resident_groups(K kernel, int nw, int variant, hipError_t* err) {
+  static std::atomic<int> cache[64][16];
   int dev = 0;
   *err = hipGetDevice(&dev);
   if (*err != hipSuccess) return 0;
-  if (dev >= 0 && dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
+  const bool cached = dev >= 0 && dev < 64 && variant >= 0 && variant < 16;
+  if (cached) {
+    const int c = cache[dev][variant].load(std::memory_order_relaxed);
     if (c > 0) return c;
   }
   hipFuncAttributes attr;
@@ -1093,7 +1164,7 @@ static int resident_groups(K kernel, int nw, hipError_t* err) {
   }
   per_cu = per_cu < 1 ? 1 : per_cu;
   const int n = per_cu * (cus > 0 ? cus : 1);
-  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  if (cached) cache[dev][variant].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -1101,10 +1172,11 @@ int decode_ranges(int cache, int D, int num_seqs, int64_t max_blocks_total, hipE
   *err = hipSuccess;
   int groups = 0;
   const bool plan = num_seqs <= kFusedPlanSeqs;
+  const int variant = (cache * 2 + (D == 128 ? 1 : 0)) * 2 + (plan ? 1 : 0);
 #define PKV_R(C_, D_)                                                                              \
   if (cache == C_ && D == D_)                                                                      \
-    groups = plan ? resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, true>, kWavesPerGroup, err) \
-                  : resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, false>, kWavesPerGroup, err);
+    groups = plan ? resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, true>, kWavesPerGroup, variant, err) \
+                  : resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, false>, kWavesPerGroup, variant, err);
   PKV_R(kF32, 64) PKV_R(kF32, 128) PKV_R(kBF16, 64) PKV_R(kBF16, 128) PKV_R(kFP8, 64) PKV_R(kFP8, 128)
 #undef PKV_R
   // one range per resident wave; workgroups in multiples of 8 (one per XCD);

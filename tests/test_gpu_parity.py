@@ -81,6 +81,19 @@ def test_ragged_lengths(cache, part):
 
 
 @pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+def test_many_ranges_per_sequence(cache):
+    """Enough blocks that every pass-1 range is busy: long sequences span many
+    ranges and workgroups, short ones share a range; no partition cuts."""
+    rng = np.random.default_rng(17 + cache)
+    lens = np.concatenate([rng.integers(1, 200, 12), rng.integers(200, 3000, 12),
+                           rng.integers(3000, 12000, 8)])
+    base = {F32: 1, BF16: 2, E4M3: 4}[cache]
+    spec = small_spec(210 + cache, base, len(lens), 32, 8, 128, lens, cache)
+    c = G.build(spec, partition_size=0)
+    full_parity(c, label=f"many ranges dtype={cache}")
+
+
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
 def test_gqa_headdim_dtype_variants(cache, D, group):
