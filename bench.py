@@ -99,16 +99,21 @@ def copy_probe(mib):
                       "launches": 3}), flush=True)
 
 
-def traffic_from_counters():
-    """HBM bytes per pass-1 launch from the committed rocprofv3 counter runs,
-    or None when the kernel source changed since they were taken."""
+def workload_key(config, partition):
+    return f"{config}:{partition}"
+
+
+def traffic_from_counters(key):
+    """HBM bytes per pass-1 launch of workload `key` from the committed
+    rocprofv3 counter runs, or None when the kernel source changed since they
+    were taken or the workload was not measured."""
     try:
         with open(COUNTERS) as f:
             c = json.load(f)
         src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
         if c.get("kernels_hip_sha256") != src:
             return None
-        return c
+        return c.get("workloads", {}).get(key)
     except (OSError, ValueError):
         return None
 
@@ -232,7 +237,7 @@ def main():
     value = kv_step / (ms_per_step * 1e-3) / 1e9
     seq_tok_s = S / (ms_per_step * 1e-3)
 
-    counters = traffic_from_counters()
+    counters = traffic_from_counters(workload_key(args.config, part))
     traffic = counters.get("hbm_bytes_per_launch") if counters else None
 
     res = {
@@ -291,6 +296,8 @@ def cpu_baseline(spec, w, bm, ids, args, pkv, torch):
     pos = np.maximum(lens - 1, 0)  # the decode token of each sampled sequence
     slots = np.array([t[i, pos[i] // BS] * BS + pos[i] % BS for i in range(k)], dtype=np.int64)
     cores = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():  # the share this job was given
+        cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
     reps = 0
     t0 = time.perf_counter()
     while True:  # repeat the sampled step until about 10 s of CPU work
