@@ -158,15 +158,18 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype
  * K and V by walking the block table):
  *   sc_t = scale * k_scale * q[s][h] . K_t
  *   out[s][h] = sum_t softmax(sc)_t * v_scale * V_t,  lse[s][h] = ln sum_t e^{sc_t}
- * The softmax is evaluated with a running maximum.  Long contexts are cut
- * into partitions of partition_size tokens, each attended independently,
- * then merged by log-sum-exp (split-KV).  L_s == 0 yields a zero row and
- * lse = -inf.
+ * The softmax is evaluated with a running maximum.  The work is cut into
+ * pieces attended independently and merged by log-sum-exp (split-KV): the
+ * (kv head, sequence, block) positions of the batch are divided into equal
+ * ranges, one per resident pass-1 wave, so a long context spans many
+ * ranges; partition_size > 0 adds a cut every partition_size tokens of each
+ * sequence.  The pieces change only the rounding order.  L_s == 0 yields a
+ * zero row and lse = -inf.
  *
  * Supported (q, cache, out) dtypes: (F32, F32, F32), (BF16, BF16, BF16),
  * (BF16, FP8_E4M3, BF16).  head_dim in {64, 128}; block_size 16;
- * 1 <= Hq / Hkv <= 16; partition_size = 0 picks a default, else a positive
- * multiple of block_size.  context_lens must lie in [0, max_context_len] and
+ * 1 <= Hq / Hkv <= 16; partition_size = 0 (no partition cuts) or a
+ * positive multiple of block_size.  context_lens must lie in [0, max_context_len] and
  * max_context_len <= max_blocks_per_seq * block_size; table entries of the
  * first ceil(L_s / 16) columns must be < num_blocks.  Other entries and slots
  * past L_s are never read (they may hold anything, NaN included).  Out-of-
@@ -181,7 +184,7 @@ typedef struct {
   int32_t block_size;
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
-  int32_t partition_size; /* tokens per split-KV partition; 0 = default */
+  int32_t partition_size; /* tokens per split-KV partition; 0 = no partition cuts */
   int64_t num_blocks;
   float scale;            /* usually 1/sqrt(head_dim) */
   float k_scale;          /* dequant scale of the K cache (1 unless fp8) */
@@ -192,14 +195,15 @@ typedef struct {
 } pkv_decode_params;
 
 /* Bytes of device workspace pkv_decode_attention needs for these params
- * (0 only for invalid params).  The workspace holds the pass-1 work list
- * built on the device from context_lens and, when a sequence can span more
- * than one partition, the per-partition fp32 partial results.  It need not be
- * initialised; it must be 256-byte aligned.  Calls that share a workspace
- * must be ordered on one stream. */
+ * (0 only for invalid params).  The workspace holds the plan built on the
+ * device from context_lens (block prefix sums) and the fp32 partial states
+ * (o, m, l, e) of split pieces; its size depends on the params, not on
+ * context_lens.  It need not be initialised; it must be 256-byte aligned.
+ * Calls that share a workspace must be ordered on one stream. */
 size_t pkv_decode_workspace_bytes(const pkv_decode_params* p);
 
-/* The partition size (tokens) the call will use for these params. */
+/* The partition size (tokens) the call will use for these params (0: no
+ * partition cuts; -1: invalid params). */
 int32_t pkv_decode_partition_size(const pkv_decode_params* p);
 
 /* Both passes: per-partition attention, then the log-sum-exp merge.
@@ -211,21 +215,24 @@ pkv_status pkv_decode_attention(const pkv_decode_params* p, void* out, const voi
                                 void* workspace, size_t workspace_bytes, float* lse_out,
                                 void* stream);
 
-/* Pass 1 alone: every (sequence, kv head, partition) attends to its
- * partition's tokens.  A sequence that fits one partition gets its final
- * out / lse here; longer ones leave fp32 partials in the workspace.  Work is
- * spread over the GPU by a device-built work list that resident workgroups
- * drain (one small planning kernel precedes the attention kernel). */
+/* Pass 1 alone: one kernel whose resident waves each attend to an equal
+ * range of the batch's blocks.  A (sequence, kv head) whose pieces all fall
+ * to one workgroup (and, with partition cuts, to one partition) gets its
+ * final out / lse here; the others leave fp32 partial states in the
+ * workspace for pass 2 (and empty sequences are left to pass 2).  Up to
+ * 1024 sequences the plan is built inside the kernel; larger batches add a
+ * one-workgroup planning kernel before it. */
 pkv_status pkv_decode_attention_partitions(const pkv_decode_params* p, void* out, const void* q,
                                            const void* k_cache, const void* v_cache,
                                            const int32_t* block_tables,
                                            const int32_t* context_lens, void* workspace,
                                            size_t workspace_bytes, float* lse_out, void* stream);
 
-/* Pass 2 alone: merges the partials pass 1 left for sequences longer than
- * one partition: M = max_p m_p, Lambda = sum_p l_p e^{m_p - M},
- * out = sum_p e^{m_p - M} o_p / Lambda, lse = M + ln Lambda.  Enqueues
- * nothing when no sequence can span two partitions. */
+/* Pass 2 alone: merges the partial states pass 1 left: M = max_p m_p,
+ * Lambda = sum_p l_p e^{m_p - M}, out = sum_p e^{m_p - M} o_p / Lambda,
+ * lse = M + ln Lambda; also writes the zero rows of empty sequences.  Must
+ * follow pass 1 of the same params, inputs and workspace on the same stream,
+ * on the same device (the range count depends on the device). */
 pkv_status pkv_decode_attention_merge(const pkv_decode_params* p, void* out,
                                       const int32_t* context_lens, const void* workspace,
                                       size_t workspace_bytes, float* lse_out, void* stream);
