@@ -101,6 +101,22 @@ pkv_status pkv_bm_fork_seq(pkv_block_manager* bm, int64_t parent, int64_t child)
 pkv_status pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n,
                                int64_t* slot_mapping_out);
 
+/* pkv_bm_append_slots with copy-on-write.  When a listed sequence's next
+ * token falls into a partially filled block that another sequence shares
+ * (after a fork inside a block), that sequence first takes a fresh block
+ * from the queue, the shared block loses one reference, and the pair is
+ * reported: copy_src_out[k] (old block), copy_dst_out[k] (new block),
+ * k < *num_copies_out, in list order.  The caller must copy those blocks on
+ * the device (pkv_copy_blocks) before writing the batch's tokens.  Sharing
+ * of physical blocks is on the pages ([P1] "PagedAttention Mechanics"; [P4]
+ * §2); resolving a write into a shared block by copying it is this library's
+ * reading.  copy_src_out / copy_dst_out hold at least n entries (host).  All
+ * or nothing; errors as pkv_bm_append_slots except that SHARED_TAIL does
+ * not occur. */
+pkv_status pkv_bm_append_slots_cow(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                                   int64_t* slot_mapping_out, int32_t* copy_src_out,
+                                   int32_t* copy_dst_out, int32_t* num_copies_out);
+
 /* Drops the sequence; each of its blocks loses one reference ([P4] §4). */
 pkv_status pkv_bm_free_seq(pkv_block_manager* bm, int64_t seq_id);
 
@@ -148,6 +164,17 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype
                                  const int64_t* slot_mapping, int32_t num_tokens,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                  int64_t num_blocks, float k_scale, float v_scale, void* stream);
+
+/* Copies whole physical blocks (K and V, every kv head, all block_size
+ * slots, bit for bit): block dst[i] <- block src[i] for i < n, e.g. the
+ * copy-on-write pairs of pkv_bm_append_slots_cow.  src, dst: device int32
+ * arrays of n entries, each in [0, num_blocks); a pair with an entry out of
+ * range is skipped; a dst that is also some src, or two equal dst, race.
+ * cache_dtype: any pkv_dtype; head_dim in {64, 128}; block_size == 16. */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                           const int32_t* src, const int32_t* dst, int32_t n,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, void* stream);
 
 /* ======================================================================== */
 /* Decode attention over the paged cache                                     */

@@ -534,6 +534,72 @@ int oracle_bm_append_slots(oracle_bm* bm, const int64_t* ids, int n, int64_t* sl
   return OR_OK;
 }
 
+/* Appending with copy-on-write.  Reading: when a token of a sequence would
+ * land inside (p % BS != 0) a block that another sequence also references,
+ * the sequence first takes the next free block in place of that one: its
+ * table entry changes to the new block, the old block keeps its other
+ * references, and (old, new) is recorded so that the caller copies the old
+ * block's contents into the new one before writing.  Everything else is as
+ * in oracle_bm_append_slots; the whole list succeeds or nothing changes. */
+int oracle_bm_append_slots_cow(oracle_bm* bm, const int64_t* ids, int n, int64_t* slots,
+                               int32_t* copy_src, int32_t* copy_dst, int32_t* num_copies) {
+  /* dry run on copies of the lengths and reference counts */
+  int need = 0;
+  int32_t* lens = (int32_t*)malloc(sizeof(int32_t) * (size_t)(bm->nseq + 1));
+  int32_t* ref = (int32_t*)malloc(sizeof(int32_t) * (size_t)bm->num_blocks);
+  for (int i = 0; i < bm->nseq; ++i) lens[i] = bm->seqs[i].len;
+  for (int b = 0; b < bm->num_blocks; ++b) ref[b] = bm->ref[b];
+  int rc = OR_OK;
+  for (int k = 0; k < n; ++k) {
+    int i = find_seq(bm, ids[k]);
+    if (i < 0) {
+      rc = OR_UNKNOWN_SEQ;
+      break;
+    }
+    int p = lens[i];
+    if (p / bm->BS >= bm->max_blocks) {
+      rc = OR_INVALID;
+      break;
+    }
+    if (p % bm->BS == 0) {
+      need += 1; /* a fresh block */
+    } else if (p == bm->seqs[i].len && ref[bm->seqs[i].table[p / bm->BS]] > 1) {
+      need += 1; /* the private copy of a shared, partly filled block */
+      ref[bm->seqs[i].table[p / bm->BS]] -= 1;
+    }
+    lens[i] = p + 1;
+  }
+  free(lens);
+  free(ref);
+  if (rc != OR_OK) return rc;
+  if (need > bm->count) return OR_OUT_OF_BLOCKS;
+  int copies = 0;
+  for (int k = 0; k < n; ++k) {
+    or_seq* q = &bm->seqs[find_seq(bm, ids[k])];
+    int p = q->len;
+    int take = p % bm->BS == 0;
+    int cow = !take && bm->ref[q->table[p / bm->BS]] > 1;
+    if (take || cow) {
+      int32_t blk = bm->fifo[bm->head];
+      bm->head = (bm->head + 1) % bm->num_blocks;
+      bm->count -= 1;
+      bm->ref[blk] = 1;
+      if (cow) {
+        int32_t old = q->table[p / bm->BS];
+        bm->ref[old] -= 1;
+        copy_src[copies] = old;
+        copy_dst[copies] = blk;
+        copies += 1;
+      }
+      q->table[p / bm->BS] = blk;
+    }
+    slots[k] = (int64_t)q->table[p / bm->BS] * bm->BS + p % bm->BS;
+    q->len = p + 1;
+  }
+  *num_copies = copies;
+  return OR_OK;
+}
+
 int oracle_bm_free_seq(oracle_bm* bm, int64_t id) {
   int i = find_seq(bm, id);
   if (i < 0) return OR_UNKNOWN_SEQ;

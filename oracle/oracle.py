@@ -74,6 +74,8 @@ def lib():
         L.oracle_bm_fork_seq.argtypes = [P, I64, I64]
         L.oracle_bm_append_slots.restype = I
         L.oracle_bm_append_slots.argtypes = [P, P, I, P]
+        L.oracle_bm_append_slots_cow.restype = I
+        L.oracle_bm_append_slots_cow.argtypes = [P, P, I, P, P, P, P]
         L.oracle_bm_free_seq.restype = I
         L.oracle_bm_free_seq.argtypes = [P, I64]
         L.oracle_bm_export.restype = I
@@ -134,6 +136,14 @@ def reshape_and_cache(k_new, v_new, src_dtype, k_cache, v_cache, cache_dtype, sl
                                         _ptr(slot_mapping), float(k_scale), float(v_scale))
     if rc != OK:
         raise ValueError(f"oracle_reshape_and_cache failed: {rc}")
+
+
+def copy_blocks(k_cache, v_cache, src, dst):
+    """Block dst[i] of both pools becomes a copy of block src[i], pair by pair
+    in order (the copy-on-write pairs)."""
+    for a, b in zip(np.asarray(src).tolist(), np.asarray(dst).tolist()):
+        k_cache[b] = k_cache[a]
+        v_cache[b] = v_cache[a]
 
 
 # ---------------------------------------------------------------- attention
@@ -209,6 +219,17 @@ class BlockAllocator:
         slots = np.full(ids.shape, -7, dtype=np.int64)
         rc = lib().oracle_bm_append_slots(self.h, _ptr(ids), ids.size, _ptr(slots))
         return rc, slots
+
+    def append_slots_cow(self, seq_ids):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        slots = np.full(ids.shape, -7, dtype=np.int64)
+        src = np.full(max(ids.size, 1), -7, dtype=np.int32)
+        dst = np.full(max(ids.size, 1), -7, dtype=np.int32)
+        n = np.zeros(1, dtype=np.int32)
+        rc = lib().oracle_bm_append_slots_cow(self.h, _ptr(ids), ids.size, _ptr(slots), _ptr(src),
+                                              _ptr(dst), _ptr(n))
+        k = int(n[0]) if rc == OK else 0
+        return rc, slots, src[:k].copy(), dst[:k].copy()
 
     def free_seq(self, sid):
         return lib().oracle_bm_free_seq(self.h, sid)

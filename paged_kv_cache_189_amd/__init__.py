@@ -33,8 +33,9 @@ PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 # every symbol include/pkv.h declares
 EXPORTED = (
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_seq", "pkv_bm_fork_seq",
-    "pkv_bm_append_slots", "pkv_bm_free_seq", "pkv_bm_export", "pkv_bm_num_free_blocks",
-    "pkv_bm_refcount", "pkv_reshape_and_cache", "pkv_decode_workspace_bytes",
+    "pkv_bm_append_slots", "pkv_bm_append_slots_cow", "pkv_bm_free_seq", "pkv_bm_export",
+    "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_reshape_and_cache", "pkv_copy_blocks",
+    "pkv_decode_workspace_bytes",
     "pkv_decode_partition_size", "pkv_decode_attention", "pkv_decode_attention_partitions",
     "pkv_decode_attention_merge", "pkv_status_string", "pkv_last_error", "pkv_version",
 )
@@ -80,11 +81,13 @@ def lib():
             "pkv_bm_add_seq": (st, [P, I64]),
             "pkv_bm_fork_seq": (st, [P, I64, I64]),
             "pkv_bm_append_slots": (st, [P, P, I32, P]),
+            "pkv_bm_append_slots_cow": (st, [P, P, I32, P, P, P, P]),
             "pkv_bm_free_seq": (st, [P, I64]),
             "pkv_bm_export": (st, [P, P, I32, P, P]),
             "pkv_bm_num_free_blocks": (I32, [P]),
             "pkv_bm_refcount": (I32, [P, I32]),
             "pkv_reshape_and_cache": (st, [P, P, st, P, P, st, P, I32, I32, I32, I32, I64, F, F, P]),
+            "pkv_copy_blocks": (st, [P, P, st, P, P, I32, I32, I32, I32, I64, P]),
             "pkv_decode_workspace_bytes": (C.c_size_t, [C.POINTER(pkv_decode_params)]),
             "pkv_decode_partition_size": (I32, [C.POINTER(pkv_decode_params)]),
             "pkv_decode_attention": (st, [C.POINTER(pkv_decode_params), P, P, P, P, P, P, P,
@@ -186,6 +189,19 @@ class BlockManager:
         rc = lib().pkv_bm_append_slots(self.h, ids.ctypes.data, ids.size, slots.ctypes.data)
         return rc, slots
 
+    def append_slots_cow(self, seq_ids, out: Optional[np.ndarray] = None):
+        """Returns (status, slots, copy_src, copy_dst): the copy-on-write pairs
+        the caller must copy on the device before writing the tokens."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        slots = out if out is not None else np.empty(ids.shape, dtype=np.int64)
+        src = np.empty(max(ids.size, 1), dtype=np.int32)
+        dst = np.empty(max(ids.size, 1), dtype=np.int32)
+        n = C.c_int32(0)
+        rc = lib().pkv_bm_append_slots_cow(self.h, ids.ctypes.data, ids.size, slots.ctypes.data,
+                                           src.ctypes.data, dst.ctypes.data, C.byref(n))
+        k = n.value if rc == PKV_OK else 0
+        return rc, slots, src[:k].copy(), dst[:k].copy()
+
     def free_seq(self, seq_id: int) -> int:
         return lib().pkv_bm_free_seq(self.h, seq_id)
 
@@ -217,6 +233,18 @@ def pkv_reshape_and_cache(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: tor
         _ptr(k_new), _ptr(v_new), dtype_code(k_new.dtype), _ptr(k_cache), _ptr(v_cache),
         dtype_code(k_cache.dtype), _ptr(slot_mapping), T, Hkv, D, 16, k_cache.shape[0],
         float(k_scale), float(v_scale), _stream(stream, k_cache)), "pkv_reshape_and_cache")
+
+
+def pkv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor,
+                    dst: torch.Tensor, stream=None):
+    """Copies physical blocks src[i] -> dst[i] (device int32 arrays) of both caches."""
+    n = src.numel()
+    if dst.numel() != n:
+        raise ValueError("src and dst differ in length")
+    _check(lib().pkv_copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache.dtype), _ptr(src), _ptr(dst), n,
+        k_cache.shape[1], v_cache.shape[2], 16, k_cache.shape[0], _stream(stream, k_cache)),
+        "pkv_copy_blocks")
 
 
 def make_decode_params(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,

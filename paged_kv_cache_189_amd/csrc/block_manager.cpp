@@ -11,7 +11,9 @@
 // Policy choices the pages leave open: free blocks are a FIFO ring seeded with
 // a caller-given order; freed blocks rejoin at the tail in table order; an
 // append batch is all-or-nothing; appending into a partially filled block that
-// is shared is refused.
+// is shared is refused by pkv_bm_append_slots, and resolved by copy-on-write
+// in pkv_bm_append_slots_cow (the sequence takes a fresh block, the caller
+// copies the shared block's contents into it on the device).
 //
 // Plain C++17 with no HIP dependency.
 #include <cstdint>
@@ -104,38 +106,57 @@ pkv_status pkv_bm_fork_seq(pkv_block_manager* bm, int64_t parent, int64_t child)
   return PKV_OK;
 }
 
-pkv_status pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n,
-                               int64_t* slot_mapping_out) {
-  if (!bm) return pkv_fail(PKV_ERR_INVALID_ARG, "pkv_bm_append_slots: NULL manager");
-  if (n < 0 || (n > 0 && (!seq_ids || !slot_mapping_out)))
-    return pkv_fail(PKV_ERR_INVALID_ARG, "pkv_bm_append_slots: bad list");
+}  // extern "C"
+
+namespace {
+
+// One append batch.  cow == false: SHARED_TAIL refuses a batch that would
+// write into a partially filled shared block.  cow == true: the first token
+// such a sequence receives takes a fresh block first; the shared block loses
+// one reference and (old, new) is reported as a copy.
+pkv_status append_batch(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                        int64_t* slot_mapping_out, bool cow, int32_t* copy_src,
+                        int32_t* copy_dst, int32_t* num_copies, const char* fn) {
+  if (!bm) return pkv_fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": NULL manager");
+  if (n < 0 || (n > 0 && (!seq_ids || !slot_mapping_out)) ||
+      (cow && (!num_copies || (n > 0 && (!copy_src || !copy_dst)))))
+    return pkv_fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": bad list");
   const int32_t BS = bm->block_size;
   // Dry run: resolve every id, count the blocks the batch takes, and check
   // that nothing would fail, before touching any state.
   std::vector<pkv_block_manager::Seq*> target(n);
   std::unordered_map<pkv_block_manager::Seq*, int32_t> pending;
+  std::unordered_map<int32_t, int32_t> released;  // references dropped by earlier copies
   int64_t need = 0;
   for (int32_t i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end())
-      return pkv_fail(PKV_ERR_UNKNOWN_SEQ, "pkv_bm_append_slots: unknown sequence id");
+      return pkv_fail(PKV_ERR_UNKNOWN_SEQ, std::string(fn) + ": unknown sequence id");
     pkv_block_manager::Seq* q = &it->second;
     target[i] = q;
     int32_t& extra = pending[q];
     int64_t p = (int64_t)q->len + extra;
     if (p / BS >= bm->max_blocks)
       return pkv_fail(PKV_ERR_INVALID_ARG,
-                      "pkv_bm_append_slots: sequence would outgrow max_blocks_per_seq");
+                      std::string(fn) + ": sequence would outgrow max_blocks_per_seq");
     if (p % BS == 0) {
       ++need;
-    } else if (extra == 0 && bm->ref[q->table[p / BS]] > 1) {
-      return pkv_fail(PKV_ERR_SHARED_TAIL,
-                      "pkv_bm_append_slots: last block is partially filled and shared");
+    } else if (extra == 0) {
+      const int32_t tail = q->table[p / BS];
+      auto rel = released.find(tail);
+      if (bm->ref[tail] - (rel == released.end() ? 0 : rel->second) > 1) {
+        if (!cow)
+          return pkv_fail(PKV_ERR_SHARED_TAIL,
+                          std::string(fn) + ": last block is partially filled and shared");
+        ++need;  // its private copy
+        ++released[tail];
+      }
     }
     ++extra;
   }
   if (need > bm->free_count)
-    return pkv_fail(PKV_ERR_OUT_OF_BLOCKS, "pkv_bm_append_slots: KV cache full");
+    return pkv_fail(PKV_ERR_OUT_OF_BLOCKS, std::string(fn) + ": KV cache full");
+  int32_t copies = 0;
   for (int32_t i = 0; i < n; ++i) {
     pkv_block_manager::Seq* q = target[i];
     int32_t p = q->len;
@@ -143,11 +164,38 @@ pkv_status pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, in
       int32_t b = bm->pop_free();
       bm->ref[b] = 1;
       q->table.push_back(b);
+    } else if (cow && bm->ref[q->table[p / BS]] > 1) {
+      const int32_t old = q->table[p / BS];
+      const int32_t b = bm->pop_free();
+      bm->ref[b] = 1;
+      bm->ref[old] -= 1;  // stays >= 1: another sequence holds it
+      q->table[p / BS] = b;
+      copy_src[copies] = old;
+      copy_dst[copies] = b;
+      ++copies;
     }
     slot_mapping_out[i] = (int64_t)q->table[p / BS] * BS + p % BS;
     q->len = p + 1;
   }
+  if (cow) *num_copies = copies;
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_bm_append_slots(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                               int64_t* slot_mapping_out) {
+  return append_batch(bm, seq_ids, n, slot_mapping_out, false, nullptr, nullptr, nullptr,
+                      "pkv_bm_append_slots");
+}
+
+pkv_status pkv_bm_append_slots_cow(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                                   int64_t* slot_mapping_out, int32_t* copy_src_out,
+                                   int32_t* copy_dst_out, int32_t* num_copies_out) {
+  return append_batch(bm, seq_ids, n, slot_mapping_out, true, copy_src_out, copy_dst_out,
+                      num_copies_out, "pkv_bm_append_slots_cow");
 }
 
 pkv_status pkv_bm_free_seq(pkv_block_manager* bm, int64_t seq_id) {

@@ -219,6 +219,31 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype
   return check_hip(e, "reshape_and_cache launch");
 }
 
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype, const int32_t* src,
+                           const int32_t* dst, int32_t n, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int64_t num_blocks, void* stream) {
+  if (n < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+    return pkv_fail(PKV_ERR_INVALID_ARG, "copy_blocks: bad sizes");
+  if (head_dim != 64 && head_dim != 128)
+    return pkv_fail(PKV_ERR_UNSUPPORTED, "copy_blocks: head_dim must be 64 or 128");
+  if (block_size != kBlockSize) return pkv_fail(PKV_ERR_UNSUPPORTED, "copy_blocks: block_size must be 16");
+  const int es = elem_bytes(cache_dtype);
+  if (es == 0) return pkv_fail(PKV_ERR_INVALID_ARG, "copy_blocks: unknown cache dtype");
+  if (n == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src || !dst) return pkv_fail(PKV_ERR_INVALID_ARG, "copy_blocks: NULL pointer");
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(src, 4) || !aligned(dst, 4))
+    return pkv_fail(PKV_ERR_INVALID_ARG, "copy_blocks: misaligned pointer");
+  pkv::CopyBlocksArgs a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.src = src;
+  a.dst = dst;
+  a.num_blocks = num_blocks;
+  a.block_bytes = (int64_t)num_kv_heads * head_dim * kBlockSize * es;
+  a.n = n;
+  return check_hip(pkv::launch_copy_blocks(a, (hipStream_t)stream), "copy_blocks launch");
+}
+
 size_t pkv_decode_workspace_bytes(const pkv_decode_params* p) {
   if (check_decode(p) != PKV_OK) return 0;
   return layout_of(*p).bytes;

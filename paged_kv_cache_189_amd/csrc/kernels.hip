@@ -220,6 +220,19 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- block copy
+// Whole physical blocks, K and V (blockIdx.y), one workgroup per pair:
+// 16-byte copies of the block's bytes (a multiple of 1 KiB).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksArgs a) {
+  const int i = blockIdx.x;
+  const int64_t src = a.src[i], dst = a.dst[i];
+  if (src < 0 || dst < 0 || src >= a.num_blocks || dst >= a.num_blocks) return;
+  char* base = static_cast<char*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
+  const u32x4* from = reinterpret_cast<const u32x4*>(base + src * a.block_bytes);
+  u32x4* to = reinterpret_cast<u32x4*>(base + dst * a.block_bytes);
+  for (int64_t k = threadIdx.x; k < a.block_bytes / 16; k += blockDim.x) to[k] = from[k];
+}
+
 // ---------------------------------------------------------------- pass 1
 template <int KIND, int D>
 struct Frags {
@@ -1110,6 +1123,12 @@ struct Depth<kFP8> {
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
+  if (a.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.n, 2), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_cache_write(const CacheWriteArgs& a, int src, int cache, int D,
                               hipStream_t stream, bool* supported) {
   *supported = true;

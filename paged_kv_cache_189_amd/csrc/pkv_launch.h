@@ -51,6 +51,18 @@ struct CacheWriteArgs {
   float v_scale;
 };
 
+struct CopyBlocksArgs {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* src;
+  const int32_t* dst;
+  int64_t num_blocks;
+  int64_t block_bytes;  // bytes of one physical block of one cache (K or V)
+  int32_t n;
+};
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+
 // Kernel variants are chosen by these codes (pkv_dtype values).
 hipError_t launch_cache_write(const CacheWriteArgs& a, int src_dtype, int cache_dtype,
                               int head_dim, hipStream_t stream, bool* supported);

@@ -51,6 +51,13 @@ def run_both(ops, num_blocks, max_blocks, order):
             res.append((r1, r2))
             if r1 == 0 and r2 == 0:
                 assert np.array_equal(s1, s2), op
+        elif kind == "append_cow":
+            r1, s1, a1, b1 = bm.append_slots_cow(op[1])
+            r2, s2, a2, b2 = ob.append_slots_cow(op[1])
+            res.append((r1, r2))
+            if r1 == 0 and r2 == 0:
+                assert np.array_equal(s1, s2), op
+                assert np.array_equal(a1, a2) and np.array_equal(b1, b2), op
         assert res[-1][0] == res[-1][1], (op, res[-1])
         assert bm.num_free() == ob.num_free()
     return bm, ob
@@ -86,6 +93,48 @@ def test_block_manager_matches_oracle_random_trace():
     assert np.array_equal(t1, t2) and np.array_equal(l1, l2)
     for b in range(nb):
         assert bm.refcount(b) == ob.refcount(b)
+
+
+@pytest.mark.parametrize("seed", [6, 7])
+def test_block_manager_cow_matches_oracle_random_trace(seed):
+    """Forks inside a block followed by copy-on-write appends, with a pool
+    small enough that OUT_OF_BLOCKS occurs: same statuses, slots, copy
+    pairs, tables, reference counts and free counts as the oracle's."""
+    rng = np.random.default_rng(seed)
+    nb, mb = 120, 30
+    order = rng.permutation(nb).astype(np.int32)
+    ops, live, nxt = [], [], 0
+    for _ in range(500):
+        u = rng.random()
+        if u < 0.1 or not live:
+            ops.append(("add", nxt))
+            live.append(nxt)
+            nxt += 1
+        elif u < 0.3:
+            ops.append(("fork", int(rng.choice(live)), nxt))
+            live.append(nxt)
+            nxt += 1
+        elif u < 0.4:
+            sid = int(rng.choice(live))
+            ops.append(("free", sid))
+            live.remove(sid)
+        elif u < 0.5:
+            ops.append(("append", rng.choice(live, size=int(rng.integers(1, 6))).astype(np.int64)))
+        else:
+            ids = rng.choice(live, size=int(rng.integers(1, 12)))
+            ops.append(("append_cow", ids.astype(np.int64)))
+    bm, ob = run_both(ops, nb, mb, order)
+    ids = np.array(sorted(live), dtype=np.int64)
+    _, t1, l1 = bm.export(ids)
+    _, t2, l2 = ob.export(ids)
+    assert np.array_equal(t1, t2) and np.array_equal(l1, l2)
+    held = np.zeros(nb, dtype=np.int64)
+    for row, L in zip(t1, l1):
+        for b in row[: -(-int(L) // BS)]:
+            held[b] += 1
+    for b in range(nb):
+        assert bm.refcount(b) == ob.refcount(b) == held[b]
+    assert bm.num_free() == int(np.sum(held == 0))
 
 
 @pytest.mark.parametrize("index", [1, 2, 3])

@@ -6,6 +6,7 @@ for fp8 KV; the oracle consumes exactly the stored (rounded / quantized)
 values the GPU consumed.  Every case prints its name before its GPU work.
 """
 import dataclasses
+import math
 
 import numpy as np
 import pytest
@@ -259,3 +260,117 @@ def test_full_size_config_sampled(index, k):
     seqs = sample_seqs(c.lens, k, index)
     full_parity(c, seqs, label=f"config {index} full size, {len(seqs)} sampled seqs")
     del c
+
+
+# ------------------------------------------------------------------- copy-on-write and multi-token append
+def _to_device(a: np.ndarray, dtype: int, device="cuda") -> torch.Tensor:
+    if dtype == BF16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def _rand_storage(gen, shape, dtype, scale=1.0):
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    if dtype == F32:
+        return x.numpy()
+    if dtype == BF16:
+        return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return (x.to(torch.bfloat16).float() / scale).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+@pytest.mark.parametrize("D", [64, 128])
+def test_copy_blocks_bit_exact(cache, D):
+    gen = torch.Generator().manual_seed(70 + cache + D)
+    nb, Hkv = 40, 4
+    ks, vs = workloads.pool_shapes(nb, Hkv, D, cache)
+    k = _rand_storage(gen, ks, cache, 0.01)
+    v = _rand_storage(gen, vs, cache, 0.01)
+    src = np.array([3, 7, 7, 0, 39, 12], dtype=np.int32)
+    dst = np.array([5, 8, 9, 1, 38, 13], dtype=np.int32)
+    dk, dv = _to_device(k, cache), _to_device(v, cache)
+    G.log(f"[copy blocks dtype={cache} D={D}]")
+    pkv.pkv_copy_blocks(dk, dv, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
+    torch.cuda.synchronize()
+    O.copy_blocks(k, v, src, dst)
+    assert np.array_equal(G.bits(G.np_storage(dk)), G.bits(k))
+    assert np.array_equal(G.bits(G.np_storage(dv)), G.bits(v))
+
+
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+def test_cow_fork_diverge_and_multi_token_append(cache):
+    """Multi-token append (one cache write of 183 tokens for three
+    sequences), forks at mid-block and block-aligned positions, then a
+    copy-on-write batch: slots and copy pairs equal the oracle allocator's,
+    both pools equal the oracle's bit for bit after the device copy and
+    cache write, and decode of all seven sequences matches the oracle."""
+    gen = torch.Generator().manual_seed(80 + cache)
+    Hq, Hkv, D, nb, mb = 16, 4, 128, 96, 24
+    qd = F32 if cache == F32 else BF16
+    ksc, vsc = (1.0, 1.0) if cache != E4M3 else (0.011, 0.013)
+    order = np.random.default_rng(81 + cache).permutation(nb).astype(np.int32)
+    bm = pkv.BlockManager(nb, BS, mb, order)
+    ob = O.BlockAllocator(nb, BS, mb, order)
+    ks, vs = workloads.pool_shapes(nb, Hkv, D, cache)
+    k = np.zeros(ks, dtype=O.NP_STORAGE[cache])
+    v = np.zeros(vs, dtype=O.NP_STORAGE[cache])
+    dk, dv = _to_device(k, cache), _to_device(v, cache)
+
+    def write(ids, with_cow):
+        if with_cow:
+            r1, s1, a1, b1 = bm.append_slots_cow(ids)
+            r2, s2, a2, b2 = ob.append_slots_cow(ids)
+            assert r1 == r2 == 0 and np.array_equal(a1, a2) and np.array_equal(b1, b2)
+            if len(a1):
+                pkv.pkv_copy_blocks(dk, dv, torch.from_numpy(a1).cuda(), torch.from_numpy(b1).cuda())
+                O.copy_blocks(k, v, a2, b2)
+        else:
+            r1, s1 = bm.append_slots(ids)
+            r2, s2 = ob.append_slots(ids)
+            assert r1 == r2 == 0
+        assert np.array_equal(s1, s2)
+        kn = _rand_storage(gen, (len(ids), Hkv, D), qd)
+        vn = _rand_storage(gen, (len(ids), Hkv, D), qd)
+        pkv.pkv_reshape_and_cache(_to_device(kn, qd), _to_device(vn, qd), dk, dv,
+                                  torch.from_numpy(s1).cuda(), ksc, vsc)
+        O.reshape_and_cache(kn, vn, qd, k, v, cache, s2, BS, ksc, vsc)
+        return len(a1) if with_cow else 0
+
+    for s in range(3):
+        assert bm.add_seq(s) == 0 and ob.add_seq(s) == 0
+    G.log(f"[cow dtype={cache}] multi-token append")
+    write(np.array([0] * 37 + [1] * 16 + [2] * 130, dtype=np.int64), False)
+    for parent, child in ((0, 3), (0, 4), (2, 5), (1, 6)):
+        assert bm.fork_seq(parent, child) == 0 and ob.fork_seq(parent, child) == 0
+    G.log(f"[cow dtype={cache}] copy-on-write batch")
+    ids = np.array([3] * 5 + [0] * 3 + [4] * 20 + [5] + [2] * 2 + [6] * 17 + [1], dtype=np.int64)
+    copies = write(ids, True)
+    # 3 then 0 copy the shared block 2 (4, its last holder, keeps it); 5 copies
+    # block 8 of 2; 6 and 1 sit at block boundaries
+    assert copies == 3
+    torch.cuda.synchronize()
+    assert np.array_equal(G.bits(G.np_storage(dk)), G.bits(k)), "K pool differs"
+    assert np.array_equal(G.bits(G.np_storage(dv)), G.bits(v)), "V pool differs"
+
+    seqs = np.arange(7, dtype=np.int64)
+    _, tables, lens = bm.export(seqs)
+    q = _rand_storage(gen, (7, Hq, D), qd)
+    dq = _to_device(q, qd)
+    out_t = torch.float32 if cache == F32 else torch.bfloat16
+    d_tables = torch.from_numpy(tables).cuda()
+    params = pkv.make_decode_params(dq, dk, d_tables, mb * BS, 1 / math.sqrt(D), ksc, vsc, out_t, 0)
+    ws = torch.empty(pkv.pkv_decode_workspace_bytes(params), dtype=torch.uint8, device="cuda")
+    out = torch.full((7, Hq, D), float("nan"), dtype=out_t, device="cuda")
+    lse = torch.full((7, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    G.log(f"[cow dtype={cache}] decode")
+    pkv.pkv_decode_attention(params, out, dq, dk, dv, d_tables, torch.from_numpy(lens).cuda(), ws, lse)
+    torch.cuda.synchronize()
+    ref, rlse = O.decode_attention(q, qd, k, v, cache, tables, lens, Hkv, BS,
+                                   float(np.float32(1 / math.sqrt(D))), ksc, vsc)
+    got = out.float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    if cache == F32:
+        assert np.all(err <= 1e-5 * np.abs(ref).max(axis=2, keepdims=True))
+    else:
+        assert err.max() <= G.TOL[cache], err.max()
+    assert np.allclose(lse.cpu().numpy(), rlse, rtol=1e-4, atol=1e-4)

@@ -463,6 +463,53 @@ def test_allocation_shared_tail_refused():
     assert rc == O.UNKNOWN_SEQ
 
 
+def test_cow_fork_inside_a_block_then_diverge():
+    """Fork in the middle of a block, then both sequences append different
+    tokens through copy-on-write: each sequence's attention equals dense
+    attention over its own logical token list (computed from the token
+    arrays, no pool or table involved), and only the first writer copies."""
+    rng = np.random.default_rng(51)
+    Hq, Hkv, D, nb = 4, 2, 16, 12
+    A = O.BlockAllocator(nb, BS, 8, rng.permutation(nb).astype(np.int32))
+    pk = np.zeros((nb, Hkv, D // 4, BS, 4), np.float32)
+    pv = np.zeros((nb, Hkv, D, BS), np.float32)
+
+    def toks(n):
+        return (rng.standard_normal((n, Hkv, D)).astype(np.float32),
+                rng.standard_normal((n, Hkv, D)).astype(np.float32))
+
+    base = toks(37)  # blocks 0, 1 full, block 2 holds 5 tokens
+    A.add_seq(0)
+    rc, slots = A.append_slots([0] * 37)
+    assert rc == O.OK
+    O.reshape_and_cache(base[0], base[1], O.F32, pk, pv, O.F32, slots, BS)
+    assert A.fork_seq(0, 1) == O.OK
+    new1, new0 = toks(10), toks(7)
+    rc, slots, src, dst = A.append_slots_cow([1] * 10 + [0] * 7)
+    assert rc == O.OK
+    _, t, lens = A.export([0, 1])
+    assert len(src) == 1 and src[0] == t[0][2] and dst[0] == t[1][2] and src[0] != dst[0]
+    assert A.refcount(int(src[0])) == 1 and A.refcount(int(dst[0])) == 1
+    assert all(A.refcount(int(b)) == 2 for b in t[0][:2])
+    O.copy_blocks(pk, pv, src, dst)
+    O.reshape_and_cache(np.concatenate([new1[0], new0[0]]), np.concatenate([new1[1], new0[1]]),
+                        O.F32, pk, pv, O.F32, slots, BS)
+    q = rng.standard_normal((2, Hq, D)).astype(np.float32)
+    scale = float(np.float32(0.25))
+    out, lse = O.decode_attention(q, O.F32, pk, pv, O.F32, t, lens, Hkv, BS, scale)
+    assert list(lens) == [44, 47]
+    for s, extra in ((0, new0), (1, new1)):
+        K = np.concatenate([base[0], extra[0]]).astype(np.float64)  # [L][Hkv][D]
+        V = np.concatenate([base[1], extra[1]]).astype(np.float64)
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            sc = K[:, g, :] @ q[s, h].astype(np.float64) * scale
+            w = np.exp(sc - sc.max())
+            ref = (w / w.sum()) @ V[:, g, :]
+            assert np.max(np.abs(out[s, h] - ref)) <= 1e-12
+            assert abs(lse[s, h] - (sc.max() + np.log(w.sum()))) <= 1e-12
+
+
 def test_allocation_freed_blocks_go_to_fifo_tail():
     """After a free, allocation drains the never-used blocks in the given
     order first, then the freed blocks in the order the table held them."""
