@@ -18,6 +18,7 @@ per launch over its HIP-event-timed average duration, against 8 TB/s.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -32,7 +33,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: KV GB/s and % of HBM peak; seq-tokens/s per layer"
 HBM_PEAK_GBS = 8000.0
-BS = 16
 COUNTERS = os.path.join(ROOT, "profiles", "pass1_hbm_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_189_amd", "csrc", "kernels.hip")
 
@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (1-5)")
     ap.add_argument("--partition", type=int, default=-1,
                     help="tokens per split-KV partition (-1: the workload's choice)")
+    ap.add_argument("--block-size", type=int, default=16, choices=(16, 32),
+                    help="tokens per physical KV block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=0,
                     help="sequences in the oracle sample (0: the default for the workload)")
@@ -65,6 +67,7 @@ def kv_bytes(spec, tables, lens):
     figure that counts shared blocks once per sequence."""
     import workloads
     per_tok = 2 * spec.num_kv_heads * spec.head_dim * workloads.ELEM_BYTES[spec.cache_dtype]
+    BS = spec.block_size
     lens = np.asarray(lens, dtype=np.int64)
     n = (lens + BS - 1) // BS
     cols = np.arange(tables.shape[1])[None, :]
@@ -81,7 +84,7 @@ def other_bytes(spec, lens):
     S = len(lens)
     qb = workloads.ELEM_BYTES[spec.q_dtype]
     ob = workloads.ELEM_BYTES[spec.out_dtype]
-    tables = 4 * int(sum(-(-int(L) // BS) for L in lens))
+    tables = 4 * int(sum(-(-int(L) // spec.block_size) for L in lens))
     return S * spec.num_q_heads * spec.head_dim * (qb + ob) + tables + 4 * S
 
 
@@ -99,8 +102,9 @@ def copy_probe(mib):
                       "launches": 3}), flush=True)
 
 
-def workload_key(config, partition):
-    return f"{config}:{partition}"
+def workload_key(config, partition, block_size=16):
+    key = f"{config}:{partition}"
+    return key if block_size == 16 else f"{key}:b{block_size}"
 
 
 def traffic_from_counters(key):
@@ -135,7 +139,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pkv.lib()
     dev = torch.device("cuda:0")
-    spec = workloads.SPECS[args.config]
+    spec = dataclasses.replace(workloads.SPECS[args.config], block_size=args.block_size)
+    BS = spec.block_size
     part = PARTITION[args.config] if args.partition < 0 else args.partition
     total_steps = args.warmup + args.steps
     lens0 = workloads.lengths(spec)
@@ -149,7 +154,8 @@ def main():
     # grow the pool for the appended tokens (fresh blocks hold N(0,1)-free garbage;
     # they are written by the cache write before they are read)
     if nb_extra:
-        ks, vs = workloads.pool_shapes(nb_extra, spec.num_kv_heads, spec.head_dim, spec.cache_dtype)
+        ks, vs = workloads.pool_shapes(nb_extra, spec.num_kv_heads, spec.head_dim, spec.cache_dtype,
+                                       BS)
         w.k_cache = torch.cat([w.k_cache, torch.zeros(ks, dtype=w.k_cache.dtype, device=dev)])
         w.v_cache = torch.cat([w.v_cache, torch.zeros(vs, dtype=w.v_cache.dtype, device=dev)])
     num_blocks = w.num_blocks + nb_extra
@@ -237,7 +243,7 @@ def main():
     value = kv_step / (ms_per_step * 1e-3) / 1e9
     seq_tok_s = S / (ms_per_step * 1e-3)
 
-    counters = traffic_from_counters(workload_key(args.config, part))
+    counters = traffic_from_counters(workload_key(args.config, part, BS))
     traffic = counters.get("hbm_bytes_per_launch") if counters else None
 
     res = {
@@ -273,6 +279,7 @@ def cpu_baseline(spec, w, bm, ids, args, pkv, torch):
     sequences' blocks are made before the clock starts."""
     from oracle import oracle as O
     import workloads
+    BS = spec.block_size
     k = min(args.cpu_seqs or CPU_SEQS[spec.index], len(ids))
     seqs = np.arange(k)
     _, tables, lens = bm.export(ids[:k])

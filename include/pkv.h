@@ -143,7 +143,8 @@ int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);
  *   context_lens  [num_seqs] int32
  *   slot_mapping  [num_tokens] int64, slot = block * block_size + offset
  * One (block, kv head) K tile keeps 16 bytes of one token's K contiguous,
- * tokens next; the V tile keeps one dimension's 16 token values contiguous.
+ * tokens next; the V tile keeps one dimension's block_size token values
+ * contiguous.  The kernels take block_size 16 or 32.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads). */
 
 /* ======================================================================== */
@@ -158,7 +159,7 @@ int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);
  * even E4M3 code of the fp32 quotient x / scale (k_scale for K, v_scale for
  * V; both > 0).  A slot < 0, or >= num_blocks * block_size, is skipped.
  * Two tokens with one slot race (the block manager never issues that).
- * head_dim in {64, 128}, block_size == 16. */
+ * head_dim in {64, 128}, block_size 16 or 32 (the pool layout's). */
 pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype src_dtype,
                                  void* k_cache, void* v_cache, pkv_dtype cache_dtype,
                                  const int64_t* slot_mapping, int32_t num_tokens,
@@ -170,7 +171,7 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype
  * copy-on-write pairs of pkv_bm_append_slots_cow.  src, dst: device int32
  * arrays of n entries, each in [0, num_blocks); a pair with an entry out of
  * range is skipped; a dst that is also some src, or two equal dst, race.
- * cache_dtype: any pkv_dtype; head_dim in {64, 128}; block_size == 16. */
+ * cache_dtype: any pkv_dtype; head_dim in {64, 128}; block_size 16 or 32. */
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype,
                            const int32_t* src, const int32_t* dst, int32_t n,
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -194,7 +195,9 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype,
  * zero row and lse = -inf.
  *
  * Supported (q, cache, out) dtypes: (F32, F32, F32), (BF16, BF16, BF16),
- * (BF16, FP8_E4M3, BF16).  head_dim in {64, 128}; block_size 16;
+ * (BF16, FP8_E4M3, BF16).  head_dim in {64, 128}; block_size 16 or 32
+ * ([P1] "Why Standard Attention Fails at Scale" gives 16 as the default;
+ * [P2] "Key Tuning Insights" tried 32 as the alternative);
  * 1 <= Hq / Hkv <= 16; partition_size = 0 (no partition cuts) or a
  * positive multiple of block_size.  context_lens must lie in [0, max_context_len] and
  * max_context_len <= max_blocks_per_seq * block_size; table entries of the

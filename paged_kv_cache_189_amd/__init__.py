@@ -231,7 +231,7 @@ def pkv_reshape_and_cache(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: tor
     T, Hkv, D = k_new.shape
     _check(lib().pkv_reshape_and_cache(
         _ptr(k_new), _ptr(v_new), dtype_code(k_new.dtype), _ptr(k_cache), _ptr(v_cache),
-        dtype_code(k_cache.dtype), _ptr(slot_mapping), T, Hkv, D, 16, k_cache.shape[0],
+        dtype_code(k_cache.dtype), _ptr(slot_mapping), T, Hkv, D, k_cache.shape[3], k_cache.shape[0],
         float(k_scale), float(v_scale), _stream(stream, k_cache)), "pkv_reshape_and_cache")
 
 
@@ -243,7 +243,8 @@ def pkv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Ten
         raise ValueError("src and dst differ in length")
     _check(lib().pkv_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache.dtype), _ptr(src), _ptr(dst), n,
-        k_cache.shape[1], v_cache.shape[2], 16, k_cache.shape[0], _stream(stream, k_cache)),
+        k_cache.shape[1], v_cache.shape[2], k_cache.shape[3], k_cache.shape[0],
+        _stream(stream, k_cache)),
         "pkv_copy_blocks")
 
 
@@ -254,7 +255,7 @@ def make_decode_params(q: torch.Tensor, k_cache: torch.Tensor, block_tables: tor
     S, Hq, D = q.shape
     p = pkv_decode_params()
     p.num_seqs, p.num_q_heads, p.num_kv_heads, p.head_dim = S, Hq, k_cache.shape[1], D
-    p.block_size = 16
+    p.block_size = k_cache.shape[3]  # [num_blocks][Hkv][D / X][block_size][X]
     p.max_blocks_per_seq = block_tables.shape[1]
     p.max_context_len = int(max_context_len)
     p.partition_size = int(partition_size)

@@ -15,7 +15,8 @@ namespace {
 
 thread_local std::string g_last_error;
 
-constexpr int32_t kBlockSize = 16;
+constexpr int32_t kTile = 16;  // tokens per pass-1 tile; blocks hold 1 or 2 tiles
+bool block_size_ok(int32_t bs) { return bs == 16 || bs == 32; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -38,8 +39,8 @@ struct Layout {
 // cuts), and ranges are at most kMaxRanges.
 Layout layout_of(const pkv_decode_params& p) {
   Layout L;
-  L.part_blocks = p.partition_size > 0 ? p.partition_size / kBlockSize : 0;
-  const int64_t max_blocks = ((int64_t)(p.max_context_len > 0 ? p.max_context_len : 0) + kBlockSize - 1) / kBlockSize;
+  L.part_blocks = p.partition_size > 0 ? p.partition_size / kTile : 0;
+  const int64_t max_blocks = ((int64_t)(p.max_context_len > 0 ? p.max_context_len : 0) + kTile - 1) / kTile;
   const int64_t pieces = L.part_blocks > 0 ? (max_blocks + L.part_blocks - 1) / L.part_blocks : 1;
   const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
   const int64_t group = p.num_kv_heads > 0 ? p.num_q_heads / p.num_kv_heads : 1;
@@ -65,11 +66,11 @@ pkv_status check_decode(const pkv_decode_params* p) {
   if (G > 16) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: query heads per kv head must be <= 16");
   if (p->head_dim != 64 && p->head_dim != 128)
     return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: head_dim must be 64 or 128");
-  if (p->block_size != kBlockSize) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: block_size must be 16");
+  if (!block_size_ok(p->block_size)) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: block_size must be 16 or 32");
   if (p->max_blocks_per_seq <= 0) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: max_blocks_per_seq must be > 0");
-  if (p->max_context_len < 0 || (int64_t)p->max_context_len > (int64_t)p->max_blocks_per_seq * kBlockSize)
+  if (p->max_context_len < 0 || (int64_t)p->max_context_len > (int64_t)p->max_blocks_per_seq * p->block_size)
     return pkv_fail(PKV_ERR_INVALID_ARG, "decode: max_context_len must be in [0, max_blocks_per_seq * block_size]");
-  if (p->partition_size < 0 || p->partition_size % kBlockSize)
+  if (p->partition_size < 0 || p->partition_size % p->block_size)
     return pkv_fail(PKV_ERR_INVALID_ARG, "decode: partition_size must be 0 or a positive multiple of block_size");
   if (p->num_blocks <= 0) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: num_blocks must be > 0");
   if (!std::isfinite(p->scale) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale) || p->k_scale <= 0.f ||
@@ -82,7 +83,7 @@ pkv_status check_decode(const pkv_decode_params* p) {
     return pkv_fail(PKV_ERR_UNSUPPORTED,
                     "decode: (q, cache, out) dtypes must be (f32,f32,f32), (bf16,bf16,bf16) or (bf16,fp8,bf16)");
   const Layout L = layout_of(*p);
-  const int64_t max_blocks = ((int64_t)p->max_context_len + kBlockSize - 1) / kBlockSize;
+  const int64_t max_blocks = ((int64_t)p->max_context_len + kTile - 1) / kTile;
   if ((int64_t)p->num_seqs * p->num_q_heads > INT32_MAX || L.max_segments * 3 > INT32_MAX ||
       (int64_t)p->num_seqs * max_blocks * p->num_kv_heads > INT32_MAX)
     return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: sequences * heads * blocks too large");
@@ -138,6 +139,7 @@ pkv_status build_args(const pkv_decode_params* p, void* out, const void* q, cons
   d.max_blocks = p->max_blocks_per_seq;
   d.max_context_len = p->max_context_len;
   d.part_blocks = L.part_blocks;
+  d.block_shift = p->block_size == 32 ? 1 : 0;
   d.num_ranges = 0;
   d.score_scale_log2 = (float)((double)p->scale * (double)p->k_scale * 1.4426950408889634);
   d.v_scale = p->v_scale;
@@ -145,8 +147,8 @@ pkv_status build_args(const pkv_decode_params* p, void* out, const void* q, cons
   // ranges of pass 1 (one per resident wave); pass 2 derives the same slots
   if (p->num_seqs > 0) {
     hipError_t e = hipSuccess;
-    d.num_ranges = pkv::decode_ranges(p->cache_dtype, p->head_dim, p->num_seqs,
-                                      (int64_t)p->num_seqs * p->num_kv_heads * ((int64_t)p->max_context_len + kBlockSize - 1) / kBlockSize,
+    d.num_ranges = pkv::decode_ranges(p->cache_dtype, p->head_dim, p->num_seqs, d.block_shift,
+                                      (int64_t)p->num_seqs * p->num_kv_heads * ((int64_t)p->max_context_len + kTile - 1) / kTile,
                                       &e);
     if (e != hipSuccess) return check_hip(e, "decode: querying the device");
   }
@@ -188,7 +190,7 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype
     return pkv_fail(PKV_ERR_INVALID_ARG, "reshape_and_cache: bad sizes");
   if (head_dim != 64 && head_dim != 128)
     return pkv_fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache: head_dim must be 64 or 128");
-  if (block_size != kBlockSize) return pkv_fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache: block_size must be 16");
+  if (!block_size_ok(block_size)) return pkv_fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache: block_size must be 16 or 32");
   const bool combo = (src_dtype == PKV_F32 && (cache_dtype == PKV_F32 || cache_dtype == PKV_BF16 ||
                                                cache_dtype == PKV_FP8_E4M3)) ||
                      (src_dtype == PKV_BF16 && (cache_dtype == PKV_BF16 || cache_dtype == PKV_FP8_E4M3));
@@ -211,6 +213,7 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype
   a.num_blocks = num_blocks;
   a.num_tokens = num_tokens;
   a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   bool ok = false;
@@ -226,7 +229,7 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype, 
     return pkv_fail(PKV_ERR_INVALID_ARG, "copy_blocks: bad sizes");
   if (head_dim != 64 && head_dim != 128)
     return pkv_fail(PKV_ERR_UNSUPPORTED, "copy_blocks: head_dim must be 64 or 128");
-  if (block_size != kBlockSize) return pkv_fail(PKV_ERR_UNSUPPORTED, "copy_blocks: block_size must be 16");
+  if (!block_size_ok(block_size)) return pkv_fail(PKV_ERR_UNSUPPORTED, "copy_blocks: block_size must be 16 or 32");
   const int es = elem_bytes(cache_dtype);
   if (es == 0) return pkv_fail(PKV_ERR_INVALID_ARG, "copy_blocks: unknown cache dtype");
   if (n == 0) return PKV_OK;
@@ -239,7 +242,7 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype, 
   a.src = src;
   a.dst = dst;
   a.num_blocks = num_blocks;
-  a.block_bytes = (int64_t)num_kv_heads * head_dim * kBlockSize * es;
+  a.block_bytes = (int64_t)num_kv_heads * head_dim * block_size * es;
   a.n = n;
   return check_hip(pkv::launch_copy_blocks(a, (hipStream_t)stream), "copy_blocks launch");
 }
@@ -251,7 +254,7 @@ size_t pkv_decode_workspace_bytes(const pkv_decode_params* p) {
 
 int32_t pkv_decode_partition_size(const pkv_decode_params* p) {
   if (check_decode(p) != PKV_OK) return -1;
-  return layout_of(*p).part_blocks * kBlockSize;
+  return layout_of(*p).part_blocks * kTile;
 }
 
 pkv_status pkv_decode_attention_partitions(const pkv_decode_params* p, void* out, const void* q, const void* k_cache,

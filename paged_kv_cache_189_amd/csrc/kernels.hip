@@ -40,7 +40,7 @@ namespace pkv {
 namespace {
 
 constexpr int kF32 = 0, kBF16 = 1, kFP8 = 2;
-constexpr int kBS = 16;  // tokens per block
+constexpr int kBS = 16;  // tokens per tile: one MFMA step; a physical block holds 1 or 2 tiles
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -160,8 +160,8 @@ __device__ __forceinline__ float load_src(const void* p, int64_t i) {
 
 // ---------------------------------------------------------------- cache write
 // One workgroup per new token; threads stride over (kv head, 16-byte chunk).
-// K chunk c of head h goes to tile[c][slot % 16][0..X); V element d goes to
-// tile[d][slot % 16].
+// With B = block_size: K chunk c of head h goes to block[h][c][slot % B][0..X);
+// V element d goes to block[h][d][slot % B].
 template <int SRC, int CACHE, int D>
 __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
   constexpr int ES = ElemSize<CACHE>::value;
@@ -169,15 +169,16 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
   constexpr int CH = D / X;
   const int t = blockIdx.x;
   const int64_t slot = a.slot_mapping[t];
-  if (slot < 0 || slot >= a.num_blocks * kBS) return;
-  const int64_t blk = slot / kBS;
-  const int off = (int)(slot % kBS);
+  const int B = a.block_size;
+  if (slot < 0 || slot >= a.num_blocks * B) return;
+  const int64_t blk = slot / B;
+  const int off = (int)(slot % B);
   for (int e = threadIdx.x; e < a.num_kv_heads * CH; e += blockDim.x) {
     const int h = e / CH, c = e % CH;
     const int64_t src0 = ((int64_t)t * a.num_kv_heads + h) * D + c * X;
     const int64_t tile = (blk * a.num_kv_heads + h);
-    const int64_t kdst = ((tile * CH + c) * kBS + off) * X;  // element index
-    const int64_t vdst = (tile * D + c * X) * kBS + off;     // element index, stride kBS
+    const int64_t kdst = ((tile * CH + c) * B + off) * X;  // element index
+    const int64_t vdst = (tile * D + c * X) * B + off;     // element index, stride B
     if constexpr (CACHE == SRC) {
       // same dtype: copy bits
       if constexpr (ES == 4) {
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
         uint32_t* vc = static_cast<uint32_t*>(a.v_cache);
         *reinterpret_cast<u32x4*>(kc + kdst) = *reinterpret_cast<const u32x4*>(ks);
 #pragma unroll
-        for (int x = 0; x < X; ++x) vc[vdst + x * kBS] = vs[x];
+        for (int x = 0; x < X; ++x) vc[vdst + x * B] = vs[x];
       } else {
         const uint16_t* ks = static_cast<const uint16_t*>(a.k_new) + src0;
         const uint16_t* vs = static_cast<const uint16_t*>(a.v_new) + src0;
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
         uint16_t* vc = static_cast<uint16_t*>(a.v_cache);
         *reinterpret_cast<u32x4*>(kc + kdst) = *reinterpret_cast<const u32x4*>(ks);
 #pragma unroll
-        for (int x = 0; x < X; ++x) vc[vdst + x * kBS] = vs[x];
+        for (int x = 0; x < X; ++x) vc[vdst + x * B] = vs[x];
       }
     } else if constexpr (CACHE == kBF16) {  // f32 -> bf16
       uint16_t* kc = static_cast<uint16_t*>(a.k_cache);
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
       for (int x = 0; x < X; ++x) kv[x] = f32_to_bf16_rne(load_src<SRC>(a.k_new, src0 + x));
       *reinterpret_cast<u32x4*>(kc + kdst) = bitcast<u32x4>(kv);
 #pragma unroll
-      for (int x = 0; x < X; ++x) vc[vdst + x * kBS] = f32_to_bf16_rne(load_src<SRC>(a.v_new, src0 + x));
+      for (int x = 0; x < X; ++x) vc[vdst + x * B] = f32_to_bf16_rne(load_src<SRC>(a.v_new, src0 + x));
     } else {  // -> fp8 E4M3 of fp32(x / scale)
       uint8_t* kc = static_cast<uint8_t*>(a.k_cache);
       uint8_t* vc = static_cast<uint8_t*>(a.v_cache);
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
       *reinterpret_cast<u32x4*>(kc + kdst) = bitcast<u32x4>(kv);
 #pragma unroll
       for (int x = 0; x < X; ++x)
-        vc[vdst + x * kBS] = f32_to_e4m3_sat(load_src<SRC>(a.v_new, src0 + x) / a.v_scale);
+        vc[vdst + x * B] = f32_to_e4m3_sat(load_src<SRC>(a.v_new, src0 + x) / a.v_scale);
     }
   }
 }
@@ -256,19 +257,43 @@ typedef const __attribute__((address_space(1))) char* gchar_p;
 template <typename T>
 using gptr = const __attribute__((address_space(1))) T*;
 
+// Lane offsets into one 16-token tile of a block of B = 16 << shift tokens:
+// K is [D/X][B][X] per (block, head), so lane l reads 16 bytes of token l % 16
+// in d-chunk 4j + l / 16; V is [D][B], lane (r, q4) reads tokens 4 q4 .. +3 of
+// dimension 16 nt + r.  Strides between the lane's loads: kj (K), vn (V).
+struct TileOffsets {
+  uint32_t koff, voff, kj, vn;
+};
 template <int KIND, int D>
-__device__ __forceinline__ void load_tile(Frags<KIND, D>& f, gchar_p kt, gchar_p vt, int lane, int r,
-                                          int q4) {
+__device__ __forceinline__ TileOffsets tile_offsets(int lane, int r, int q4, int shift) {
+  using T = Tile<KIND, D>;
+  const uint32_t B = 16u << shift;
+  TileOffsets o;
+  o.koff = (((uint32_t)lane >> 4) * B + ((uint32_t)lane & 15u)) * 16u;
+  o.voff = ((uint32_t)r * B + 4u * (uint32_t)q4) * T::ES;
+  o.kj = 64u * B;
+  o.vn = 16u * B * T::ES;
+  return o;
+}
+
+// With 32-token blocks a tile reads half of each V row (and of each 128-byte
+// K line pair); the other half is the next tile's, read one stage later, so
+// those loads keep the default cache policy and find it in L2.
+template <int KIND, int D, bool STREAM>
+__device__ __forceinline__ void load_tile(Frags<KIND, D>& f, gchar_p kt, gchar_p vt,
+                                          const TileOffsets& o) {
   using T = Tile<KIND, D>;
   using V = typename T::V;
-  const uint32_t koff = (uint32_t)lane * 16u;
-  const uint32_t voff = (uint32_t)(r * kBS + 4 * q4) * T::ES;
 #pragma unroll
-  for (int j = 0; j < T::NK; ++j)
-    f.k[j] = __builtin_nontemporal_load(reinterpret_cast<gptr<u32x4>>(kt + koff + j * 1024));
+  for (int j = 0; j < T::NK; ++j) {
+    gptr<u32x4> p = reinterpret_cast<gptr<u32x4>>(kt + j * o.kj + o.koff);
+    f.k[j] = STREAM ? __builtin_nontemporal_load(p) : *p;
+  }
 #pragma unroll
-  for (int nt = 0; nt < T::NT; ++nt)
-    f.v[nt] = __builtin_nontemporal_load(reinterpret_cast<gptr<V>>(vt + voff + nt * 16 * kBS * T::ES));
+  for (int nt = 0; nt < T::NT; ++nt) {
+    gptr<V> p = reinterpret_cast<gptr<V>>(vt + nt * o.vn + o.voff);
+    f.v[nt] = STREAM ? __builtin_nontemporal_load(p) : *p;
+  }
 }
 
 // Read-only inputs of pass 1 (tables, lengths, the plan) seen through the
@@ -498,7 +523,7 @@ struct FoldLds {
 // (the same pair's piece in the next range) and merge it in.  publish >= 0:
 // instead of writing, hand the state to the previous range's wave through
 // fold[publish] and raise flag[publish].
-template <int KIND, int D, int S>
+template <int KIND, int D, int S, int SH>
 __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D>& qs,
                                                FoldLds<KIND, D>* fold, int* flag, int s, int g,
                                                int b_begin, int b_end, int slot, int done,
@@ -535,19 +560,24 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
     }
   }
 
+  // Tile b (16 tokens) lies in table entry b >> shift, half b & 1 of a
+  // 32-token block.
+  constexpr int shift = SH;
   const cptr<int32_t> tbl = as_const(a.block_tables) + (int64_t)s * a.max_blocks;
-  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)g * T::BYTES;
-  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)g * T::BYTES;
-  const int64_t bstride = (int64_t)a.num_kv_heads * T::BYTES;
+  const char* kbase = static_cast<const char*>(a.k_cache) + ((int64_t)g * T::BYTES << shift);
+  const char* vbase = static_cast<const char*>(a.v_cache) + ((int64_t)g * T::BYTES << shift);
+  const int64_t bstride = (int64_t)a.num_kv_heads * T::BYTES << shift;
   const int64_t last_block = a.num_blocks - 1;
+  const TileOffsets toff = tile_offsets<KIND, D>(lane, r, q4, shift);
 
   // Tile bases are wave-uniform: keep them in scalar registers so each load
   // is a scalar base plus the lane's 32-bit offset.
   auto tile_of = [&](int b, gchar_p& kt, gchar_p& vt) {
-    int64_t phys = __builtin_amdgcn_readfirstlane(tbl[b]);
+    int64_t phys = __builtin_amdgcn_readfirstlane(tbl[b >> shift]);
     phys = phys < 0 ? 0 : (phys > last_block ? last_block : phys);
-    kt = uniform_ptr(kbase + phys * bstride);
-    vt = uniform_ptr(vbase + phys * bstride);
+    const int half = b & ((1 << shift) - 1);
+    kt = uniform_ptr(kbase + phys * bstride + half * (kBS * 16));
+    vt = uniform_ptr(vbase + phys * bstride + half * (kBS * T::ES));
   };
 
   // S rotating register buffers: while block b is processed, the loads of
@@ -562,7 +592,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
     gchar_p kt, vt;
 #define PKV_PREFETCH(BUF, AHEAD)                          \
   tile_of(min(b + (AHEAD)*NW, b_end - 1), kt, vt);        \
-  load_tile<KIND, D>(BUF, kt, vt, lane, r, q4);
+  load_tile<KIND, D, SH == 0>(BUF, kt, vt, toff);
 #define PKV_STAGE(CUR, NXT)                                              \
   PKV_PREFETCH(NXT, S - 1)                                               \
   process_block<KIND, D>(st, CUR, qs, b, L, a.score_scale_log2, lane, q4);   \
@@ -784,7 +814,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
 // workgroup 0 also stores them for pass 2.  Otherwise decode_plan_kernel
 // has built them beforehand.
 constexpr int kFusedPlanSeqs = 1024;
-template <int KIND, int D, int NW, int S, bool PLAN>
+template <int KIND, int D, int NW, int S, bool PLAN, int SH>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_partitions_kernel(DecodeArgs a) {
   __shared__ QLds<KIND, D> qs[NW];
@@ -876,7 +906,7 @@ void decode_partitions_kernel(DecodeArgs a) {
     const bool absorb = fold_on && ps + hi == x1 && hi < nblk && w != NW - 1;
     const bool whole = fold_on ? lo == 0 && range_of(pe - 1, total, R) / NW == rg / NW : lo == 0 && hi == nblk;
     const int slot = g * PT + cp(s) + pidx + rg;
-    decode_segment<KIND, D, S>(a, qs[w], fold, flag, s, g, lo, hi, whole ? -1 : slot,
+    decode_segment<KIND, D, S, SH>(a, qs[w], fold, flag, s, g, lo, hi, whole ? -1 : slot,
                                (int)(x - x_first), (int)(x1 - x_first), absorb ? w : -1,
                                publish ? w - 1 : -1);
     x = ps + hi;
@@ -1150,18 +1180,18 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, int src, int cache, int D
 }
 
 // Workgroups of `kernel` (NW waves each) that fit on the current device at
-// once, cached per device and kernel variant (`variant` < 16 names it).  Computed from the kernel's
+// once, cached per device and kernel variant (`variant` < 32 names it).  Computed from the kernel's
 // register and LDS use against gfx950's limits (512 VGPRs per SIMD lane with
 // the accumulation registers unified, 160 KiB LDS and at most 8 waves per
 // SIMD): the runtime's occupancy query assumes 256 VGPRs here and would
 // leave two thirds of the GPU idle for a 168-register kernel.
 template <typename K>
 static int resident_groups(K kernel, int nw, int variant, hipError_t* err) {
-  static std::atomic<int> cache[64][16];
+  static std::atomic<int> cache[64][32];
   int dev = 0;
   *err = hipGetDevice(&dev);
   if (*err != hipSuccess) return 0;
-  const bool cached = dev >= 0 && dev < 64 && variant >= 0 && variant < 16;
+  const bool cached = dev >= 0 && dev < 64 && variant >= 0 && variant < 32;
   if (cached) {
     const int c = cache[dev][variant].load(std::memory_order_relaxed);
     if (c > 0) return c;
@@ -1187,16 +1217,19 @@ static int resident_groups(K kernel, int nw, int variant, hipError_t* err) {
   return n;
 }
 
-int decode_ranges(int cache, int D, int num_seqs, int64_t max_blocks_total, hipError_t* err) {
+int decode_ranges(int cache, int D, int num_seqs, int block_shift, int64_t max_blocks_total,
+                  hipError_t* err) {
   *err = hipSuccess;
   int groups = 0;
   const bool plan = num_seqs <= kFusedPlanSeqs;
-  const int variant = (cache * 2 + (D == 128 ? 1 : 0)) * 2 + (plan ? 1 : 0);
-#define PKV_R(C_, D_)                                                                              \
-  if (cache == C_ && D == D_)                                                                      \
-    groups = plan ? resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, true>, kWavesPerGroup, variant, err) \
-                  : resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, false>, kWavesPerGroup, variant, err);
-  PKV_R(kF32, 64) PKV_R(kF32, 128) PKV_R(kBF16, 64) PKV_R(kBF16, 128) PKV_R(kFP8, 64) PKV_R(kFP8, 128)
+  const int variant = ((cache * 2 + (D == 128 ? 1 : 0)) * 2 + (plan ? 1 : 0)) * 2 + block_shift;
+#define PKV_R(C_, D_, SH_)                                                                              \
+  if (cache == C_ && D == D_ && block_shift == SH_)                                                     \
+    groups = plan ? resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, true, SH_>, kWavesPerGroup, variant, err) \
+                  : resident_groups(decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, false, SH_>, kWavesPerGroup, variant, err);
+  PKV_R(kF32, 64, 0) PKV_R(kF32, 128, 0) PKV_R(kBF16, 64, 0) PKV_R(kBF16, 128, 0) PKV_R(kFP8, 64, 0)
+  PKV_R(kFP8, 128, 0) PKV_R(kF32, 64, 1) PKV_R(kF32, 128, 1) PKV_R(kBF16, 64, 1) PKV_R(kBF16, 128, 1)
+  PKV_R(kFP8, 64, 1) PKV_R(kFP8, 128, 1)
 #undef PKV_R
   // one range per resident wave; workgroups in multiples of 8 (one per XCD);
   // never more ranges than the blocks that can exist
@@ -1214,22 +1247,23 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int cache, int D, hipSt
   if (a.num_seqs == 0) return hipSuccess;
   const int block = kWavesPerGroup * 64;
   const dim3 grid(a.num_ranges / kWavesPerGroup);
-#define PKV_P1(C_, D_)                                                                          \
-  if (cache == C_ && D == D_) {                                                                 \
+#define PKV_P1(C_, D_, SH_)                                                                     \
+  if (cache == C_ && D == D_ && a.block_shift == SH_) {                                         \
     if (a.num_seqs <= kFusedPlanSeqs) {                                                         \
-      hipLaunchKernelGGL((decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, true>), \
+      hipLaunchKernelGGL((decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, true, SH_>), \
                          grid, dim3(block), 0, stream, a);                                      \
       return hipGetLastError();                                                                 \
     }                                                                                           \
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, a);                  \
     hipError_t err = hipGetLastError();                                                         \
     if (err != hipSuccess) return err;                                                          \
-    hipLaunchKernelGGL((decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, false>), \
+    hipLaunchKernelGGL((decode_partitions_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, false, SH_>), \
                        grid, dim3(block), 0, stream, a);                                        \
     return hipGetLastError();                                                                   \
   }
-  PKV_P1(kF32, 64) PKV_P1(kF32, 128) PKV_P1(kBF16, 64) PKV_P1(kBF16, 128) PKV_P1(kFP8, 64)
-  PKV_P1(kFP8, 128)
+  PKV_P1(kF32, 64, 0) PKV_P1(kF32, 128, 0) PKV_P1(kBF16, 64, 0) PKV_P1(kBF16, 128, 0)
+  PKV_P1(kFP8, 64, 0) PKV_P1(kFP8, 128, 0) PKV_P1(kF32, 64, 1) PKV_P1(kF32, 128, 1)
+  PKV_P1(kBF16, 64, 1) PKV_P1(kBF16, 128, 1) PKV_P1(kFP8, 64, 1) PKV_P1(kFP8, 128, 1)
 #undef PKV_P1
   *supported = false;
   return hipSuccess;

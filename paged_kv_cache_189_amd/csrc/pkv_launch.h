@@ -32,7 +32,8 @@ struct DecodeArgs {
   int32_t group;
   int32_t max_blocks;
   int32_t max_context_len;
-  int32_t part_blocks;  // blocks per partition (0: cut only at range starts)
+  int32_t part_blocks;  // 16-token tiles per partition (0: cut only at range starts)
+  int32_t block_shift;  // log2(block_size / 16): tiles per physical block = 1 << block_shift
   int32_t num_ranges;   // pass-1 waves, one range each (a multiple of 8 * waves per group)
   float score_scale_log2;  // scale * k_scale * log2(e)
   float v_scale;
@@ -47,6 +48,7 @@ struct CacheWriteArgs {
   int64_t num_blocks;
   int32_t num_tokens;
   int32_t num_kv_heads;
+  int32_t block_size;  // tokens per physical block (16 or 32)
   float k_scale;
   float v_scale;
 };
@@ -77,8 +79,9 @@ constexpr int kWavesPerGroup = 4;
 constexpr int kMaxRanges = 16384;
 
 // Pass-1 ranges (one per resident wave) for a cache dtype / head dim / batch
-// size on the current device, capped by the number of blocks that can exist.
-int decode_ranges(int cache_dtype, int head_dim, int num_seqs, int64_t max_blocks_total,
-                  hipError_t* err);
+// size / block shift on the current device, capped by the number of 16-token
+// tiles that can exist.
+int decode_ranges(int cache_dtype, int head_dim, int num_seqs, int block_shift,
+                  int64_t max_blocks_total, hipError_t* err);
 
 }  // namespace pkv

@@ -238,7 +238,10 @@ def test_workspace_and_partition_sizing():
     (dict(num_q_heads=6, num_kv_heads=4), pkv.PKV_ERR_INVALID_ARG),
     (dict(num_q_heads=34, num_kv_heads=2), pkv.PKV_ERR_UNSUPPORTED),
     (dict(head_dim=96), pkv.PKV_ERR_UNSUPPORTED),
-    (dict(block_size=32), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(block_size=64), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(block_size=8), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(block_size=32, partition_size=48), pkv.PKV_ERR_INVALID_ARG),
+    (dict(block_size=32, max_context_len=64 * 32 + 1), pkv.PKV_ERR_INVALID_ARG),
     (dict(max_context_len=64 * 16 + 1), pkv.PKV_ERR_INVALID_ARG),
     (dict(partition_size=100), pkv.PKV_ERR_INVALID_ARG),
     (dict(k_scale=0.0), pkv.PKV_ERR_INVALID_ARG),

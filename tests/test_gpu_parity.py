@@ -374,3 +374,67 @@ def test_cow_fork_diverge_and_multi_token_append(cache):
     else:
         assert err.max() <= G.TOL[cache], err.max()
     assert np.allclose(lse.cpu().numpy(), rlse, rtol=1e-4, atol=1e-4)
+
+
+# ------------------------------------------------------------------- 32-token blocks
+@pytest.mark.parametrize("cache,D", [(F32, 128), (BF16, 128), (BF16, 64), (E4M3, 128)])
+@pytest.mark.parametrize("part", [0, 64])
+def test_block_size_32(cache, D, part):
+    """32-token blocks: one multi-token append + cache write (bit-exact
+    against the oracle's cache write) and decode against the oracle, for
+    lengths around the block and tile boundaries."""
+    BS32 = 32
+    gen = torch.Generator().manual_seed(90 + cache + D + part)
+    Hq, Hkv = 16, 4
+    lens = np.array([1, 15, 16, 17, 31, 32, 33, 100, 1000, 3000], dtype=np.int64)
+    nb = int(sum(-(-lens // BS32))) + 7
+    mb = int(-(-lens.max() // BS32))
+    qd = F32 if cache == F32 else BF16
+    ksc, vsc = (1.0, 1.0) if cache != E4M3 else (0.011, 0.013)
+    order = np.random.default_rng(91 + cache).permutation(nb).astype(np.int32)
+    bm = pkv.BlockManager(nb, BS32, mb, order)
+    ob = O.BlockAllocator(nb, BS32, mb, order)
+    ks, vs = workloads.pool_shapes(nb, Hkv, D, cache, BS32)
+    k = _rand_storage(gen, ks, cache, ksc)  # unused slots keep random values
+    v = _rand_storage(gen, vs, cache, vsc)
+    dk, dv = _to_device(k, cache), _to_device(v, cache)
+    S = len(lens)
+    for s in range(S):
+        assert bm.add_seq(s) == 0 and ob.add_seq(s) == 0
+    ids = np.repeat(np.arange(S, dtype=np.int64), lens)
+    r1, s1 = bm.append_slots(ids)
+    r2, s2 = ob.append_slots(ids)
+    assert r1 == r2 == 0 and np.array_equal(s1, s2)
+    kn = _rand_storage(gen, (len(ids), Hkv, D), qd)
+    vn = _rand_storage(gen, (len(ids), Hkv, D), qd)
+    G.log(f"[block 32 dtype={cache} D={D} part={part}] cache write of {len(ids)} tokens")
+    pkv.pkv_reshape_and_cache(_to_device(kn, qd), _to_device(vn, qd), dk, dv,
+                              torch.from_numpy(s1).cuda(), ksc, vsc)
+    O.reshape_and_cache(kn, vn, qd, k, v, cache, s2, BS32, ksc, vsc)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.bits(G.np_storage(dk)), G.bits(k)), "K pool differs"
+    assert np.array_equal(G.bits(G.np_storage(dv)), G.bits(v)), "V pool differs"
+    _, tables, blens = bm.export(np.arange(S, dtype=np.int64))
+    q = _rand_storage(gen, (S, Hq, D), qd)
+    dq = _to_device(q, qd)
+    out_t = torch.float32 if cache == F32 else torch.bfloat16
+    d_tables = torch.from_numpy(tables).cuda()
+    params = pkv.make_decode_params(dq, dk, d_tables, mb * BS32, 1 / math.sqrt(D), ksc, vsc, out_t,
+                                    part)
+    assert params.block_size == BS32
+    ws = torch.empty(pkv.pkv_decode_workspace_bytes(params), dtype=torch.uint8, device="cuda")
+    out = torch.full((S, Hq, D), float("nan"), dtype=out_t, device="cuda")
+    lse = torch.full((S, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    G.log(f"[block 32 dtype={cache} D={D} part={part}] decode")
+    pkv.pkv_decode_attention(params, out, dq, dk, dv, d_tables, torch.from_numpy(blens).cuda(), ws,
+                             lse)
+    torch.cuda.synchronize()
+    ref, rlse = O.decode_attention(q, qd, k, v, cache, tables, blens, Hkv, BS32,
+                                   float(np.float32(1 / math.sqrt(D))), ksc, vsc)
+    got = out.float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    if cache == F32:
+        assert np.all(err <= 1e-5 * np.abs(ref).max(axis=2, keepdims=True))
+    else:
+        assert err.max() <= G.TOL[cache], err.max()
+    assert np.allclose(lse.cpu().numpy(), rlse, rtol=1e-4, atol=1e-4)

@@ -51,6 +51,7 @@ class Spec:
     pool_blocks: Optional[int] = None  # fixed pool size; None = needed + 10% slack
     partition_size: int = 0         # 0 = library default
     max_model_len: int = 0          # table width in tokens; 0 = max length rounded up
+    block_size: int = BLOCK         # tokens per physical block (16 or 32)
 
     @property
     def group(self) -> int:
@@ -106,10 +107,11 @@ def lengths(spec: Spec, num_seqs: Optional[int] = None) -> np.ndarray:
 
 
 def blocks_needed(spec: Spec, lens: np.ndarray) -> int:
+    B = spec.block_size
     if spec.prefix_tokens:
-        pre = spec.prefix_tokens // BLOCK
-        return pre + int(sum(-(-(int(L) - spec.prefix_tokens) // BLOCK) for L in lens))
-    return int(sum(-(-int(L) // BLOCK) for L in lens))
+        pre = spec.prefix_tokens // B
+        return pre + int(sum(-(-(int(L) - spec.prefix_tokens) // B) for L in lens))
+    return int(sum(-(-int(L) // B) for L in lens))
 
 
 def pool_blocks(spec: Spec, lens: np.ndarray) -> int:
@@ -120,7 +122,7 @@ def pool_blocks(spec: Spec, lens: np.ndarray) -> int:
 
 def max_blocks_per_seq(spec: Spec, lens: np.ndarray) -> int:
     width = spec.max_model_len or int(lens.max())
-    return -(-width // BLOCK)
+    return -(-width // spec.block_size)
 
 
 def free_order(spec: Spec, num_blocks: int) -> np.ndarray:
@@ -209,9 +211,9 @@ def _amax_bf16(seed: int, n: int, device) -> float:
     return float(m.item())
 
 
-def pool_shapes(num_blocks, H, D, cache_dtype):
+def pool_shapes(num_blocks, H, D, cache_dtype, block_size=BLOCK):
     X = 16 // ELEM_BYTES[cache_dtype]
-    return (num_blocks, H, D // X, BLOCK, X), (num_blocks, H, D, BLOCK)
+    return (num_blocks, H, D // X, block_size, X), (num_blocks, H, D, block_size)
 
 
 @dataclasses.dataclass
@@ -222,8 +224,8 @@ class Workload:
     max_blocks: int
     free_order: np.ndarray
     q: torch.Tensor             # [S][Hq][D] storage dtype
-    k_cache: torch.Tensor       # [nb][Hkv][D/X][16][X]
-    v_cache: torch.Tensor       # [nb][Hkv][D][16]
+    k_cache: torch.Tensor       # [nb][Hkv][D/X][block_size][X]
+    v_cache: torch.Tensor       # [nb][Hkv][D][block_size]
     k_new: torch.Tensor         # [S][Hkv][D] (f32 or bf16)
     v_new: torch.Tensor
     k_scale: float
@@ -241,7 +243,7 @@ def make(spec: Spec, device="cpu", num_seqs: Optional[int] = None,
     nb = pool_blocks(spec, lens)
     mb = max_blocks_per_seq(spec, lens)
     Hq, Hkv, D = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
-    kshape, vshape = pool_shapes(nb, Hkv, D, spec.cache_dtype)
+    kshape, vshape = pool_shapes(nb, Hkv, D, spec.cache_dtype, spec.block_size)
     new_dtype = torch.float32 if spec.q_dtype == F32 else torch.bfloat16
     pool_n = int(np.prod(kshape))
     new_n = S * Hkv * D
@@ -279,9 +281,10 @@ def poison_unused(w: Workload, tables: np.ndarray, filled: np.ndarray):
     sequence's filled length in its blocks.  `filled` is tokens held per
     sequence before the decode token is written."""
     nb = w.num_blocks
+    B = w.spec.block_size
     used = np.zeros(nb, dtype=bool)
     for s in range(len(filled)):
-        n = -(-int(filled[s]) // BLOCK)
+        n = -(-int(filled[s]) // B)
         used[tables[s, :n]] = True
     val = poison_value(w.spec.cache_dtype)
     dev = w.k_cache.device
@@ -292,7 +295,7 @@ def poison_unused(w: Workload, tables: np.ndarray, filled: np.ndarray):
     # tail slots of each sequence's last (partial) block; shared prefix blocks are full
     for s in range(len(filled)):
         L = int(filled[s])
-        if L % BLOCK:
-            b = int(tables[s, L // BLOCK])
-            w.k_cache[b, :, :, L % BLOCK:, :] = val
-            w.v_cache[b, :, :, L % BLOCK:] = val
+        if L % B:
+            b = int(tables[s, L // B])
+            w.k_cache[b, :, :, L % B:, :] = val
+            w.v_cache[b, :, :, L % B:] = val
