@@ -398,6 +398,88 @@ int oracle_decode_attention_split(int num_seqs, int num_q_heads, int num_kv_head
 }
 
 /* ------------------------------------------------------------------------ */
+/* Chunked prefill over the paged cache.  The pages name chunked prefill as */
+/* an engine setting ([P2]; [P3] Step 2) and give no formula.  Reading:      */
+/* sequence s holds L_s tokens in the cache, and the last                    */
+/* C_s = qstart[s+1] - qstart[s] of them are this step's query chunk (their  */
+/* K and V already written).  Query row i = qstart[s] + j, 0 <= j < C_s, is  */
+/* the token at position p = L_s - C_s + j and attends causally to tokens    */
+/* 0..p:                                                                      */
+/*   sc_t = scale * sum_d q[i][h][d] * k_scale * K(t)[d],   t <= p            */
+/*   out[i][h] = sum_t softmax(sc)_t * v_scale * V(t),  lse = ln sum e^{sc}   */
+/* (GQA as in decode: query head h reads kv head h / (Hq / Hkv)).  A row with */
+/* p < 0 (a chunk longer than the context) gets a zero row and lse = -inf.    */
+/* fp64 from the exactly widened stored values; with C_s = 1 this is decode. */
+/* ------------------------------------------------------------------------ */
+int oracle_prefill_attention(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_blocks_per_seq, int q_dtype, const void* q,
+                             int cache_dtype, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const int32_t* query_start, float scale, float k_scale,
+                             float v_scale, double* out, double* lse, int num_threads) {
+  problem p = {num_seqs,   num_q_heads, num_kv_heads, head_dim,     block_size,
+               max_blocks_per_seq, q_dtype, cache_dtype, q, k_cache, v_cache,
+               block_tables, context_lens, (double)scale, (double)k_scale, (double)v_scale};
+  int rc = check_problem(&p);
+  if (rc) return rc;
+  if (query_start[0] != 0) return OR_INVALID;
+  for (int s = 0; s < num_seqs; ++s)
+    if (query_start[s + 1] < query_start[s]) return OR_INVALID;
+  const int64_t rows = query_start[num_seqs];
+  int32_t* seq_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)(rows > 0 ? rows : 1));
+  for (int s = 0; s < num_seqs; ++s)
+    for (int64_t i = query_start[s]; i < query_start[s + 1]; ++i) seq_of[i] = s;
+  const int G = num_q_heads / num_kv_heads;
+  const int64_t X = 16 / elem_bytes(cache_dtype);
+  const int64_t pairs = rows * num_q_heads;
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+#pragma omp parallel for schedule(dynamic, 4)
+#endif
+  for (int64_t k = 0; k < pairs; ++k) {
+    const int64_t i = k / num_q_heads;
+    const int h = (int)(k % num_q_heads), g = h / G;
+    const int s = seq_of[i];
+    const int C = query_start[s + 1] - query_start[s];
+    const int pos = context_lens[s] - C + (int)(i - query_start[s]);
+    double* o = out + k * head_dim;
+    for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
+    if (pos < 0) {
+      lse[k] = -INFINITY;
+      continue;
+    }
+    const int n = pos + 1;
+    double* sc = (double*)malloc(sizeof(double) * (size_t)n);
+    for (int t = 0; t < n; ++t) {
+      const int64_t b = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
+      const int64_t off = t % block_size;
+      double acc = 0.0;
+      for (int d = 0; d < head_dim; ++d) {
+        double qd = widen(q_dtype, q, (i * num_q_heads + h) * head_dim + d);
+        double kd = widen(cache_dtype, k_cache,
+                          k_index(b, g, off, d, num_kv_heads, head_dim, block_size, X)) *
+                    p.k_scale;
+        acc += qd * kd;
+      }
+      sc[t] = p.scale * acc;
+    }
+    double m = -INFINITY;
+    for (int t = 0; t < n; ++t)
+      if (sc[t] > m) m = sc[t];
+    double sum = 0.0;
+    for (int t = 0; t < n; ++t) sum += exp(sc[t] - m);
+    for (int t = 0; t < n; ++t) {
+      const double w = exp(sc[t] - m) / sum;
+      for (int d = 0; d < head_dim; ++d) o[d] += w * v_at(&p, s, g, t, d);
+    }
+    lse[k] = m + log(sum);
+    free(sc);
+  }
+  free(seq_of);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Block allocation ([P1] PagedAttention Mechanics: a new token is appended  */
 /* to its sequence and a physical page is taken only when the sequence needs */
 /* one; several sequences may point at the same physical pages; [P4] §4:    */

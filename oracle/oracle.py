@@ -65,6 +65,9 @@ def lib():
         L.oracle_decode_attention_split.restype = I
         L.oracle_decode_attention_split.argtypes = [I, I, I, I, I, I, I, P, I, P, P, P, P, F, F,
                                                     F, I, P, P, I]
+        L.oracle_prefill_attention.restype = I
+        L.oracle_prefill_attention.argtypes = [I, I, I, I, I, I, I, P, I, P, P, P, P, P, F, F, F,
+                                               P, P, I]
         L.oracle_bm_create.restype = P
         L.oracle_bm_create.argtypes = [I, I, I, P]
         L.oracle_bm_destroy.argtypes = [P]
@@ -183,6 +186,28 @@ def decode_attention_split(q, q_dtype, k_cache, v_cache, cache_dtype, block_tabl
         float(k_scale), float(v_scale), int(partition_tokens), _ptr(out), _ptr(lse), threads)
     if rc != OK:
         raise ValueError(f"oracle_decode_attention_split failed: {rc}")
+    return out, lse
+
+
+def prefill_attention(q, q_dtype, k_cache, v_cache, cache_dtype, block_tables, context_lens,
+                      query_start, num_kv_heads, block_size, scale, k_scale=1.0, v_scale=1.0,
+                      threads=0):
+    """fp64 chunked-prefill attention.  q: [rows][Hq][D] storage array (rows =
+    query_start[-1]).  Returns (out [rows][Hq][D], lse [rows][Hq])."""
+    R, Hq, D = q.shape
+    S = len(context_lens)
+    block_tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    context_lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    query_start = np.ascontiguousarray(query_start, dtype=np.int32)
+    assert query_start.shape == (S + 1,) and query_start[-1] == R
+    out = np.zeros((R, Hq, D), dtype=np.float64)
+    lse = np.zeros((R, Hq), dtype=np.float64)
+    rc = lib().oracle_prefill_attention(
+        S, Hq, num_kv_heads, D, block_size, block_tables.shape[1], q_dtype, _ptr(q), cache_dtype,
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), _ptr(query_start),
+        float(scale), float(k_scale), float(v_scale), _ptr(out), _ptr(lse), threads)
+    if rc != OK:
+        raise ValueError(f"oracle_prefill_attention failed: {rc}")
     return out, lse
 
 

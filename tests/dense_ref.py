@@ -90,3 +90,38 @@ def sdpa_attention(q, q_dtype, k_cache, v_cache, cache_dtype, tables, lens, scal
             Q[s][:, None, :], K, V, scale=float(scale))
         out[s] = o[:, 0, :].numpy()
     return out
+
+
+def dense_prefill(q, q_dtype, k_cache, v_cache, cache_dtype, tables, lens, qstart, scale,
+                  k_scale=1.0, v_scale=1.0):
+    """Chunked prefill as matrices: for sequence s, Q_s [C][Hq][D] against the
+    gathered K/V [L][Hkv][D] with the boolean mask t <= L - C + j."""
+    R, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    scale, k_scale, v_scale = (f32(x) for x in (scale, k_scale, v_scale))
+    Q = decode_np(q, q_dtype)
+    out = np.zeros((R, Hq, D))
+    lse = np.full((R, Hq), -np.inf)
+    for s in range(len(lens)):
+        L = int(lens[s])
+        a, b = int(qstart[s]), int(qstart[s + 1])
+        C = b - a
+        if C == 0 or L == 0:
+            continue
+        Ks, Vs = gather(k_cache, v_cache, tables[s], L)
+        Kf = np.repeat(decode_np(Ks, cache_dtype) * float(k_scale), G, axis=1)  # [L][Hq][D]
+        Vf = np.repeat(decode_np(Vs, cache_dtype) * float(v_scale), G, axis=1)
+        pos = L - C + np.arange(C)                                      # [C]
+        mask = np.arange(L)[None, :] <= pos[:, None]                     # [C][L]
+        sc = np.einsum("jhd,thd->hjt", Q[a:b], Kf) * float(scale)        # [Hq][C][L]
+        sc = np.where(mask[None], sc, -np.inf)
+        m = sc.max(axis=2, keepdims=True)
+        live = np.isfinite(m)
+        e = np.where(live, np.exp(sc - np.where(live, m, 0.0)), 0.0)
+        z = e.sum(axis=2, keepdims=True)
+        w = np.divide(e, z, out=np.zeros_like(e), where=z > 0)
+        out[a:b] = np.einsum("hjt,thd->jhd", w, Vf)
+        with np.errstate(divide="ignore"):
+            lse[a:b] = np.where(z[..., 0] > 0, m[..., 0] + np.log(z[..., 0]), -np.inf).T
+    return out, lse

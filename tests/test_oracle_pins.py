@@ -528,3 +528,84 @@ def test_allocation_freed_blocks_go_to_fifo_tail():
     assert rc == O.OK and A.num_free() == 0
     got = [int(slots[j * BS]) // BS for j in range(nb - 2)]
     assert got == list(order[5:]) + freed
+
+
+# ----------------------------------------------------------------- chunked prefill
+def prefill_problem(seed, lens, chunks, **kw):
+    p = make_problem(seed, lens, **kw)
+    rng = np.random.default_rng(seed + 1000)
+    qstart = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    Hq, D = p["q"].shape[1], p["q"].shape[2]
+    p["q"] = rand_storage(rng, (int(qstart[-1]), Hq, D), p["q_dtype"])
+    p["query_start"] = qstart
+    return p
+
+
+def prefill_args(p):
+    return dict(q=p["q"], q_dtype=p["q_dtype"], k_cache=p["k_cache"], v_cache=p["v_cache"],
+                cache_dtype=p["cache_dtype"], block_tables=p["block_tables"],
+                context_lens=p["context_lens"], query_start=p["query_start"],
+                num_kv_heads=p["num_kv_heads"], block_size=p["block_size"], scale=p["scale"],
+                k_scale=p["k_scale"], v_scale=p["v_scale"])
+
+
+@pytest.mark.parametrize("cache_dtype,q_dtype", [(O.F32, O.F32), (O.BF16, O.BF16), (O.E4M3, O.BF16)])
+def test_prefill_equals_dense_causal(cache_dtype, q_dtype):
+    ks = 0.02 if cache_dtype == O.E4M3 else 1.0
+    p = prefill_problem(61, [40, 17, 100, 5], [40, 3, 37, 1], cache_dtype=cache_dtype,
+                        q_dtype=q_dtype, k_scale=ks, v_scale=ks)
+    out, lse = O.prefill_attention(**prefill_args(p))
+    ref, rlse = dense_ref.dense_prefill(p["q"], q_dtype, p["k_cache"], p["v_cache"], cache_dtype,
+                                        p["block_tables"], p["context_lens"], p["query_start"],
+                                        p["scale"], ks, ks)
+    assert np.max(np.abs(out - ref)) <= 1e-12
+    assert np.max(np.abs(lse - rlse)) <= 1e-12
+
+
+def test_prefill_full_sequence_is_causal_self_attention():
+    """C = L: every token of the sequence is a query; torch's causal SDPA
+    (fp64, KV heads repeated over their group) gives the same rows."""
+    p = prefill_problem(62, [33, 70], [33, 70], cache_dtype=O.F32, q_dtype=O.F32, Hq=8, Hkv=2,
+                        D=32)
+    out, _ = O.prefill_attention(**prefill_args(p))
+    qs = p["query_start"]
+    for s in range(2):
+        L = int(p["context_lens"][s])
+        Ks, Vs = dense_ref.gather(p["k_cache"], p["v_cache"], p["block_tables"][s], L)
+        Kt = torch.from_numpy(Ks.astype(np.float64)).repeat_interleave(4, dim=1).permute(1, 0, 2)
+        Vt = torch.from_numpy(Vs.astype(np.float64)).repeat_interleave(4, dim=1).permute(1, 0, 2)
+        Qt = torch.from_numpy(p["q"][qs[s]:qs[s + 1]].astype(np.float64)).permute(1, 0, 2)
+        r = torch.nn.functional.scaled_dot_product_attention(Qt, Kt, Vt, is_causal=True,
+                                                             scale=dense_ref.f32(p["scale"]))
+        assert np.max(np.abs(out[qs[s]:qs[s + 1]] - r.permute(1, 0, 2).numpy())) <= 1e-12
+
+
+def test_prefill_single_token_chunk_is_decode():
+    p = prefill_problem(63, [1, 16, 17, 300], [1, 1, 1, 1])
+    out, lse = O.prefill_attention(**prefill_args(p))
+    d_out, d_lse = O.decode_attention(p["q"], p["q_dtype"], p["k_cache"], p["v_cache"],
+                                      p["cache_dtype"], p["block_tables"], p["context_lens"],
+                                      p["num_kv_heads"], BS, p["scale"])
+    assert np.array_equal(out, d_out) and np.array_equal(lse, d_lse)
+
+
+def test_prefill_two_chunks_equal_one():
+    """Queries [a, b) in one call equal [a, m) with the context cut at m,
+    then [m, b): the position bookkeeping L - C + j agrees."""
+    p = prefill_problem(64, [90], [50])
+    whole, wl = O.prefill_attention(**prefill_args(p))
+    first = dict(prefill_args(p), q=np.ascontiguousarray(p["q"][:20]),
+                 context_lens=np.array([60], np.int32), query_start=np.array([0, 20], np.int32))
+    second = dict(prefill_args(p), q=np.ascontiguousarray(p["q"][20:]),
+                  query_start=np.array([0, 30], np.int32))
+    o1, l1 = O.prefill_attention(**first)
+    o2, l2 = O.prefill_attention(**second)
+    assert np.array_equal(np.concatenate([o1, o2]), whole)
+    assert np.array_equal(np.concatenate([l1, l2]), wl)
+
+
+def test_prefill_chunk_longer_than_context_rows_are_empty():
+    p = prefill_problem(65, [3], [5])
+    out, lse = O.prefill_attention(**prefill_args(p))
+    assert np.all(out[:2] == 0) and np.all(np.isneginf(lse[:2]))
+    assert np.all(np.isfinite(lse[2:]))
