@@ -268,6 +268,50 @@ pkv_status pkv_decode_attention_merge(const pkv_decode_params* p, void* out,
                                       size_t workspace_bytes, float* lse_out, void* stream);
 
 /* ======================================================================== */
+/* Chunked prefill attention over the paged cache                            */
+/* ======================================================================== */
+/* Attention for a chunk of new tokens per sequence (chunked prefill, named
+ * as an engine setting in [P2] and [P3] Step 2; the pages give no formula).
+ * Sequence s holds L_s = context_lens[s] tokens in the cache, the last
+ * C_s = query_start[s+1] - query_start[s] of which are its chunk (their K
+ * and V already written, e.g. by pkv_reshape_and_cache of all C_s tokens).
+ * Query row i = query_start[s] + j (0 <= j < C_s) is the token at position
+ * p = L_s - C_s + j and attends causally to tokens 0..p:
+ *   sc_t = scale * k_scale * q[i][h] . K_t (t <= p)
+ *   out[i][h] = sum_t softmax(sc)_t * v_scale * V_t,  lse[i][h] = ln sum_t e^{sc_t}
+ * With C_s = 1 this is decode.  A row with p < 0 (C_s > L_s) gets a zero row
+ * and lse = -inf.  q, out: [num_query_tokens][Hq][D] (rows packed by
+ * sequence); lse_out: NULL or [num_query_tokens][Hq] fp32.
+ * query_start: device int32 [num_seqs + 1], non-decreasing, query_start[0]
+ * = 0 and query_start[num_seqs] = num_query_tokens (not checked: it lives
+ * on the device).  Other fields, dtypes and limits as pkv_decode_params;
+ * num_seqs <= 1024.  No workspace: every (kv head, sequence, tile of
+ * 16 / G query tokens) is one wave that walks the table up to its last
+ * row's position. */
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;
+  int32_t num_query_tokens;
+  int64_t num_blocks;
+  float scale;
+  float k_scale;
+  float v_scale;
+  int32_t q_dtype;
+  int32_t cache_dtype;
+  int32_t out_dtype;
+} pkv_prefill_params;
+
+pkv_status pkv_prefill_attention(const pkv_prefill_params* p, void* out, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 const int32_t* query_start, float* lse_out, void* stream);
+
+/* ======================================================================== */
 /* Diagnostics                                                               */
 /* ======================================================================== */
 const char* pkv_status_string(pkv_status s);

@@ -37,7 +37,8 @@ EXPORTED = (
     "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_reshape_and_cache", "pkv_copy_blocks",
     "pkv_decode_workspace_bytes",
     "pkv_decode_partition_size", "pkv_decode_attention", "pkv_decode_attention_partitions",
-    "pkv_decode_attention_merge", "pkv_status_string", "pkv_last_error", "pkv_version",
+    "pkv_decode_attention_merge", "pkv_prefill_attention", "pkv_status_string",
+    "pkv_last_error", "pkv_version",
 )
 
 
@@ -57,6 +58,16 @@ class pkv_decode_params(C.Structure):
         ("num_seqs", C.c_int32), ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
         ("head_dim", C.c_int32), ("block_size", C.c_int32), ("max_blocks_per_seq", C.c_int32),
         ("max_context_len", C.c_int32), ("partition_size", C.c_int32), ("num_blocks", C.c_int64),
+        ("scale", C.c_float), ("k_scale", C.c_float), ("v_scale", C.c_float),
+        ("q_dtype", C.c_int32), ("cache_dtype", C.c_int32), ("out_dtype", C.c_int32),
+    ]
+
+
+class pkv_prefill_params(C.Structure):
+    _fields_ = [
+        ("num_seqs", C.c_int32), ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+        ("head_dim", C.c_int32), ("block_size", C.c_int32), ("max_blocks_per_seq", C.c_int32),
+        ("max_context_len", C.c_int32), ("num_query_tokens", C.c_int32), ("num_blocks", C.c_int64),
         ("scale", C.c_float), ("k_scale", C.c_float), ("v_scale", C.c_float),
         ("q_dtype", C.c_int32), ("cache_dtype", C.c_int32), ("out_dtype", C.c_int32),
     ]
@@ -96,6 +107,8 @@ def lib():
                                                      P, P, C.c_size_t, P, P]),
             "pkv_decode_attention_merge": (st, [C.POINTER(pkv_decode_params), P, P, P, C.c_size_t,
                                                 P, P]),
+            "pkv_prefill_attention": (st, [C.POINTER(pkv_prefill_params), P, P, P, P, P, P, P,
+                                           P, P]),
             "pkv_status_string": (C.c_char_p, [st]),
             "pkv_last_error": (C.c_char_p, []),
             "pkv_version": (C.c_char_p, []),
@@ -309,3 +322,34 @@ def pkv_decode_attention_merge(params, out, context_lens, workspace=None, lse=No
 
 def pkv_version() -> str:
     return lib().pkv_version().decode()
+
+
+# ------------------------------------------------------------------ chunked prefill
+def make_prefill_params(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
+                        num_seqs: int, max_context_len: int, scale: float, k_scale: float = 1.0,
+                        v_scale: float = 1.0,
+                        out_dtype: Optional[torch.dtype] = None) -> pkv_prefill_params:
+    R, Hq, D = q.shape
+    p = pkv_prefill_params()
+    p.num_seqs, p.num_q_heads, p.num_kv_heads, p.head_dim = num_seqs, Hq, k_cache.shape[1], D
+    p.block_size = k_cache.shape[3]
+    p.max_blocks_per_seq = block_tables.shape[1]
+    p.max_context_len = int(max_context_len)
+    p.num_query_tokens = R
+    p.num_blocks = k_cache.shape[0]
+    p.scale, p.k_scale, p.v_scale = float(scale), float(k_scale), float(v_scale)
+    p.q_dtype = dtype_code(q.dtype)
+    p.cache_dtype = dtype_code(k_cache.dtype)
+    p.out_dtype = dtype_code(out_dtype if out_dtype is not None else q.dtype)
+    return p
+
+
+def pkv_prefill_attention(params: pkv_prefill_params, out: torch.Tensor, q: torch.Tensor,
+                          k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor,
+                          query_start: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                          stream=None):
+    _check(lib().pkv_prefill_attention(
+        C.byref(params), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start), _ptr(lse), _stream(stream, out)),
+        "pkv_prefill_attention")

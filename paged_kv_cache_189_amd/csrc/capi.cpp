@@ -257,6 +257,67 @@ int32_t pkv_decode_partition_size(const pkv_decode_params* p) {
   return layout_of(*p).part_blocks * kTile;
 }
 
+pkv_status pkv_prefill_attention(const pkv_prefill_params* p, void* out, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                 const int32_t* query_start, float* lse_out, void* stream) {
+  if (!p) return pkv_fail(PKV_ERR_INVALID_ARG, "prefill: params is NULL");
+  // the shared checks of the decode parameters, then the prefill ones
+  pkv_decode_params d{};
+  d.num_seqs = p->num_seqs;
+  d.num_q_heads = p->num_q_heads;
+  d.num_kv_heads = p->num_kv_heads;
+  d.head_dim = p->head_dim;
+  d.block_size = p->block_size;
+  d.max_blocks_per_seq = p->max_blocks_per_seq;
+  d.max_context_len = p->max_context_len;
+  d.partition_size = 0;
+  d.num_blocks = p->num_blocks;
+  d.scale = p->scale;
+  d.k_scale = p->k_scale;
+  d.v_scale = p->v_scale;
+  d.q_dtype = p->q_dtype;
+  d.cache_dtype = p->cache_dtype;
+  d.out_dtype = p->out_dtype;
+  pkv_status st = check_decode(&d);
+  if (st != PKV_OK) return st;
+  if (p->num_query_tokens < 0) return pkv_fail(PKV_ERR_INVALID_ARG, "prefill: num_query_tokens < 0");
+  if (p->num_seqs > pkv::kPrefillMaxSeqs)
+    return pkv_fail(PKV_ERR_UNSUPPORTED, "prefill: at most 1024 sequences per call");
+  if ((int64_t)p->num_query_tokens * p->num_q_heads > INT32_MAX)
+    return pkv_fail(PKV_ERR_UNSUPPORTED, "prefill: query tokens * heads too large");
+  if (p->num_seqs == 0 || p->num_query_tokens == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return pkv_fail(PKV_ERR_INVALID_ARG, "prefill: NULL pointer");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4) ||
+      (lse_out && !aligned(lse_out, 4)))
+    return pkv_fail(PKV_ERR_INVALID_ARG, "prefill: misaligned pointer");
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.lse = lse_out;
+  a.num_blocks = p->num_blocks;
+  a.num_seqs = p->num_seqs;
+  a.num_q_heads = p->num_q_heads;
+  a.num_kv_heads = p->num_kv_heads;
+  a.group = p->num_q_heads / p->num_kv_heads;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.max_context_len = p->max_context_len;
+  a.tokens_per_tile = 16 / a.group;
+  a.block_shift = p->block_size == 32 ? 1 : 0;
+  a.score_scale_log2 = (float)((double)p->scale * (double)p->k_scale * 1.4426950408889634);
+  a.v_scale = p->v_scale;
+  bool ok = false;
+  hipError_t e = pkv::launch_prefill(a, p->cache_dtype, p->head_dim, p->num_query_tokens, (hipStream_t)stream, &ok);
+  if (!ok) return pkv_fail(PKV_ERR_UNSUPPORTED, "prefill: no kernel variant");
+  return check_hip(e, "prefill launch");
+}
+
 pkv_status pkv_decode_attention_partitions(const pkv_decode_params* p, void* out, const void* q, const void* k_cache,
                                            const void* v_cache, const int32_t* block_tables,
                                            const int32_t* context_lens, void* workspace, size_t workspace_bytes,

@@ -454,10 +454,15 @@ struct RunState {
   }
 };
 
-// Scores, online softmax and P.V for logical block b of the sequence.
+// Scores, online softmax and P.V for tile b (16 tokens) of the sequence.  L:
+// tokens the lane's query row may see (per lane for causal prefill rows);
+// Lv: tokens of the sequence (wave-uniform).  Scores past L get weight 0;
+// V rows past Lv may hold anything (NaN too) and are selected away.  In the
+// P.V product a lane holds V of dimension r, not query row r, so V masking
+// uses the sequence bound only.
 template <int KIND, int D>
 __device__ __forceinline__ void process_block(RunState<KIND, D>& st, const Frags<KIND, D>& f,
-                                              const QLds<KIND, D>& q, int b, int L,
+                                              const QLds<KIND, D>& q, int b, int L, int Lv,
                                               float score_scale_log2, int lane, int q4) {
   using T = Tile<KIND, D>;
   const f32x4 sc = scores<KIND, D>(f, q, lane);
@@ -486,10 +491,14 @@ __device__ __forceinline__ void process_block(RunState<KIND, D>& st, const Frags
   const Weights<KIND> wt = make_weights<KIND>(p);
   st.l += wt.used;
   st.e += wt.exact;
-  if ((b + 1) * kBS > L)
-    accumulate_pv<KIND, D, true>(st.acc, f, wt, valid);
-  else
+  if ((b + 1) * kBS > Lv) {
+    bool vvalid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vvalid[i] = tok0 + i < Lv;
+    accumulate_pv<KIND, D, true>(st.acc, f, wt, vvalid);
+  } else {
     accumulate_pv<KIND, D, false>(st.acc, f, wt, valid);
+  }
 }
 
 // A SIMD issues for its oldest wave first, so waves given equal work finish
@@ -595,7 +604,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
   load_tile<KIND, D, SH == 0>(BUF, kt, vt, toff);
 #define PKV_STAGE(CUR, NXT)                                              \
   PKV_PREFETCH(NXT, S - 1)                                               \
-  process_block<KIND, D>(st, CUR, qs, b, L, a.score_scale_log2, lane, q4);   \
+  process_block<KIND, D>(st, CUR, qs, b, L, L, a.score_scale_log2, lane, q4); \
   pace(done + (b - b_begin), total);                                     \
   b += NW;                                                               \
   if (b >= b_end) break;
@@ -1123,6 +1132,159 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   if (tid == 0 && a.lse) a.lse[row] = Ex > 0.f ? (M + __builtin_amdgcn_logf(Ex)) * kLn2 : -INFINITY;
 }
 
+// ---------------------------------------------------------------- chunked prefill
+// One wave per (kv head g, sequence s, query tile): a tile holds
+// tokens_per_tile = 16 / G query tokens of the chunk, row r = token r / G,
+// head r % G, so the G heads of a token share the K/V tile as in decode.
+// Row r's query token sits at position p = L - C + j of its sequence and sees
+// tokens 0..p (causal); the wave walks tiles up to its last row's position.
+// Rows past the chunk copy the tile's last row and are not written; rows
+// with p < 0 (chunk longer than the context) are written as zeros.
+template <int KIND, int D, int S, int SH>
+__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, QLds<KIND, D>& qs, int s, int g,
+                                             int qt) {
+  using T = Tile<KIND, D>;
+  constexpr int NW = 1;
+  constexpr int shift = SH;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, q4 = lane >> 4;
+  const int G = a.group, NQ = a.tokens_per_tile, Hq = a.num_q_heads;
+  const cptr<int32_t> qst = as_const(a.query_start);
+  const int q0 = qst[s], C = qst[s + 1] - q0;
+  int Ls = as_const(a.context_lens)[s];
+  Ls = Ls < 0 ? 0 : (Ls > a.max_context_len ? a.max_context_len : Ls);
+  const int jl = r / G, hh = r % G;
+  const int j = qt * NQ + jl;
+  const bool row_ok = r < NQ * G && j < C;
+  const int jlast = (qt * NQ + NQ < C ? qt * NQ + NQ : C) - 1;
+  const int jj = row_ok ? j : jlast;
+  const int Lrow = Ls - C + jj + 1;            // tokens this row sees (<= 0: none)
+  const int Lmax = Ls - C + jlast + 1;         // wave-uniform: the tile's last row
+  const int L = Lrow > 1 ? Lrow : 1;           // empty rows look at token 0, then write zeros
+
+  u32x4 qreg[T::NQ];
+  {
+    constexpr int QES = KIND == kF32 ? 4 : 2;
+    const gchar_p qrow = (gchar_p) static_cast<const char*>(a.q) +
+                         ((int64_t)(q0 + jj) * Hq + g * G + hh) * D * QES;
+#pragma unroll
+    for (int jq = 0; jq < T::NQ; ++jq) {
+      int off;
+      if constexpr (KIND == kFP8)
+        off = ((jq >> 1) * 4 + q4) * 32 + (jq & 1) * 16;
+      else
+        off = (jq * 4 + q4) * 16;
+      qreg[jq] = *reinterpret_cast<gptr<u32x4>>(qrow + off);
+    }
+  }
+
+  const cptr<int32_t> tbl = as_const(a.block_tables) + (int64_t)s * a.max_blocks;
+  const char* kbase = static_cast<const char*>(a.k_cache) + ((int64_t)g * T::BYTES << shift);
+  const char* vbase = static_cast<const char*>(a.v_cache) + ((int64_t)g * T::BYTES << shift);
+  const int64_t bstride = (int64_t)a.num_kv_heads * T::BYTES << shift;
+  const int64_t last_block = a.num_blocks - 1;
+  const TileOffsets toff = tile_offsets<KIND, D>(lane, r, q4, shift);
+  auto tile_of = [&](int b, gchar_p& kt, gchar_p& vt) {
+    int64_t phys = __builtin_amdgcn_readfirstlane(tbl[b >> shift]);
+    phys = phys < 0 ? 0 : (phys > last_block ? last_block : phys);
+    const int half = b & ((1 << shift) - 1);
+    kt = uniform_ptr(kbase + phys * bstride + half * (kBS * 16));
+    vt = uniform_ptr(vbase + phys * bstride + half * (kBS * T::ES));
+  };
+
+  RunState<KIND, D> st;
+  st.init();
+  const int b_end = Lmax > 0 ? (Lmax + kBS - 1) / kBS : 0;
+  int b = 0;
+  if (b < b_end) {
+    Frags<KIND, D> f0, f1, f2, f3;
+    gchar_p kt, vt;
+#define PKV_PREFETCH(BUF, AHEAD)                          \
+  tile_of(min(b + (AHEAD)*NW, b_end - 1), kt, vt);        \
+  load_tile<KIND, D, SH == 0>(BUF, kt, vt, toff);
+#define PKV_STAGE(CUR, NXT)                                                     \
+  PKV_PREFETCH(NXT, S - 1)                                                      \
+  process_block<KIND, D>(st, CUR, qs, b, L, Lmax, a.score_scale_log2, lane, q4); \
+  b += NW;                                                                      \
+  if (b >= b_end) break;
+    PKV_PREFETCH(f0, 0)
+    if constexpr (S >= 3) { PKV_PREFETCH(f1, 1) }
+    if constexpr (S >= 4) { PKV_PREFETCH(f2, 2) }
+#pragma unroll
+    for (int jq = 0; jq < T::NQ; ++jq) qs.qf[jq][lane] = qreg[jq];
+    if constexpr (S == 2) {
+      for (;;) { PKV_STAGE(f0, f1) PKV_STAGE(f1, f0) }
+    } else if constexpr (S == 3) {
+      for (;;) { PKV_STAGE(f0, f2) PKV_STAGE(f1, f0) PKV_STAGE(f2, f1) }
+    } else {
+      for (;;) { PKV_STAGE(f0, f3) PKV_STAGE(f1, f0) PKV_STAGE(f2, f1) PKV_STAGE(f3, f2) }
+    }
+#undef PKV_STAGE
+#undef PKV_PREFETCH
+  }
+  const float l_run = sum_across_groups(st.l);
+  const float e_run = sum_across_groups(st.e);
+  if (!row_ok) return;
+  const bool empty = Lrow <= 0;
+  const int64_t row = (int64_t)(q0 + j) * Hq + g * G + hh;
+  const float inv = !empty && l_run > 0.f ? a.v_scale / l_run : 0.f;
+#pragma unroll
+  for (int nt = 0; nt < T::NT; ++nt) {
+    const int d = nt * 16 + 4 * q4;
+    const f32x4 o = st.acc.o[nt] * inv;
+    if constexpr (KIND == kF32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d) = o;
+    } else {
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * D + d) = u32x2{lo, hi};
+    }
+  }
+  if (q4 == 0 && a.lse)
+    a.lse[row] = !empty && e_run > 0.f ? (st.m + __builtin_amdgcn_logf(e_run)) * kLn2 : -INFINITY;
+}
+
+// Items (g, s, tile) lie head major: item g * TQ + ct[s] + tile, ct = prefix
+// sums of the sequences' tile counts, built in LDS by every workgroup.
+// Workgroup b takes items ((b mod 8) * (nWG / 8) + b / 8) * NW + w, so one XCD
+// works through consecutive tiles of the same sequences and shares their K/V
+// tiles in its L2.
+template <int KIND, int D, int NW, int S, int SH>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(PrefillArgs a) {
+  __shared__ QLds<KIND, D> qs[NW];
+  __shared__ int lct[kPrefillMaxSeqs + 1];
+  __shared__ int wsums[NW];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nseq = a.num_seqs, H = a.num_kv_heads, NQ = a.tokens_per_tile;
+  {
+    const int tid = threadIdx.x;
+    int carry = 0;
+    for (int c0 = 0; c0 < nseq; c0 += NW * 64) {
+      const int s = c0 + tid;
+      int C = s < nseq ? a.query_start[s + 1] - a.query_start[s] : 0;
+      C = C < 0 ? 0 : C;
+      int tot;
+      const int e = block_exclusive_scan<NW>((C + NQ - 1) / NQ, wsums, &tot);
+      if (s < nseq) lct[s] = carry + e;
+      carry += tot;
+    }
+    if (tid == 0) lct[nseq] = carry;
+    __syncthreads();
+  }
+  const int TQ = lct[nseq];
+  const int groups = gridDim.x;
+  const int64_t k = ((int64_t)(blockIdx.x & 7) * (groups >> 3) + (blockIdx.x >> 3)) * NW + w;
+  if (k >= (int64_t)H * TQ) return;
+  const int g = (int)(k / TQ), rem = (int)(k % TQ);
+  int lo = 0, hi = nseq;  // largest s with lct[s] <= rem
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (lct[mid] <= rem) lo = mid; else hi = mid;
+  }
+  prefill_tile<KIND, D, S, SH>(a, qs[w], lo, g, rem - lct[lo]);
+}
+
 // Register buffers (prefetch depth + 1) per cache dtype, at two waves per
 // SIMD (eight per CU).  Three measured the same as two buffers at three
 // waves per SIMD, and leave registers for the fold merge.
@@ -1265,6 +1427,33 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int cache, int D, hipSt
   PKV_P1(kFP8, 64, 0) PKV_P1(kFP8, 128, 0) PKV_P1(kF32, 64, 1) PKV_P1(kF32, 128, 1)
   PKV_P1(kBF16, 64, 1) PKV_P1(kBF16, 128, 1) PKV_P1(kFP8, 64, 1) PKV_P1(kFP8, 128, 1)
 #undef PKV_P1
+  *supported = false;
+  return hipSuccess;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int cache, int D, int64_t num_rows,
+                          hipStream_t stream, bool* supported) {
+  *supported = true;
+  if (a.num_seqs == 0 || num_rows == 0) return hipSuccess;
+  // waves: at most one per query tile, tiles <= rows / tokens_per_tile + one partial per sequence
+  const int64_t tiles = (num_rows + a.tokens_per_tile - 1) / a.tokens_per_tile + a.num_seqs;
+  int64_t groups = ((int64_t)a.num_kv_heads * tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+  groups = (groups + 7) / 8 * 8;
+  if (groups > INT32_MAX) {
+    *supported = false;
+    return hipSuccess;
+  }
+  const dim3 grid((unsigned)groups), block(kWavesPerGroup * 64);
+#define PKV_PF(C_, D_, SH_)                                                                   \
+  if (cache == C_ && D == D_ && a.block_shift == SH_) {                                       \
+    hipLaunchKernelGGL((prefill_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, SH_>), grid, \
+                       block, 0, stream, a);                                                  \
+    return hipGetLastError();                                                                 \
+  }
+  PKV_PF(kF32, 64, 0) PKV_PF(kF32, 128, 0) PKV_PF(kBF16, 64, 0) PKV_PF(kBF16, 128, 0)
+  PKV_PF(kFP8, 64, 0) PKV_PF(kFP8, 128, 0) PKV_PF(kF32, 64, 1) PKV_PF(kF32, 128, 1)
+  PKV_PF(kBF16, 64, 1) PKV_PF(kBF16, 128, 1) PKV_PF(kFP8, 64, 1) PKV_PF(kFP8, 128, 1)
+#undef PKV_PF
   *supported = false;
   return hipSuccess;
 }

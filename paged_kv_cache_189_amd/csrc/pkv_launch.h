@@ -39,6 +39,36 @@ struct DecodeArgs {
   float v_scale;
 };
 
+// Chunked prefill: the query rows of sequence s are
+// [query_start[s], query_start[s+1]), the last tokens of its context.
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;  // [S + 1]
+  float* lse;                  // [rows][Hq] or null
+  int64_t num_blocks;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t max_blocks;
+  int32_t max_context_len;
+  int32_t tokens_per_tile;  // query tokens sharing one 16-row MFMA tile: 16 / group
+  int32_t block_shift;
+  float score_scale_log2;
+  float v_scale;
+};
+
+// Largest batch the prefill kernel plans in LDS.
+constexpr int kPrefillMaxSeqs = 1024;
+
+hipError_t launch_prefill(const PrefillArgs& a, int cache_dtype, int head_dim, int64_t num_rows,
+                          hipStream_t stream, bool* supported);
+
 struct CacheWriteArgs {
   const void* k_new;
   const void* v_new;

@@ -438,3 +438,99 @@ def test_block_size_32(cache, D, part):
     else:
         assert err.max() <= G.TOL[cache], err.max()
     assert np.allclose(lse.cpu().numpy(), rlse, rtol=1e-4, atol=1e-4)
+
+
+# ------------------------------------------------------------------- chunked prefill
+def _paged_batch(gen, cache, D, Hkv, lens, bs=16, seed=0):
+    """Pools filled through one multi-token append + cache write on both sides
+    (bit-exact check included); returns device and host views."""
+    lens = np.asarray(lens, dtype=np.int64)
+    nb = int(sum(-(-lens // bs))) + 5
+    mb = int(max(1, -(-lens.max() // bs)))
+    qd = F32 if cache == F32 else BF16
+    ksc, vsc = (1.0, 1.0) if cache != E4M3 else (0.011, 0.013)
+    order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+    bm = pkv.BlockManager(nb, bs, mb, order)
+    ob = O.BlockAllocator(nb, bs, mb, order)
+    ks, vs = workloads.pool_shapes(nb, Hkv, D, cache, bs)
+    k = _rand_storage(gen, ks, cache, ksc)
+    v = _rand_storage(gen, vs, cache, vsc)
+    dk, dv = _to_device(k, cache), _to_device(v, cache)
+    S = len(lens)
+    for s in range(S):
+        assert bm.add_seq(s) == 0 and ob.add_seq(s) == 0
+    ids = np.repeat(np.arange(S, dtype=np.int64), lens)
+    r1, s1 = bm.append_slots(ids)
+    r2, s2 = ob.append_slots(ids)
+    assert r1 == r2 == 0 and np.array_equal(s1, s2)
+    kn = _rand_storage(gen, (len(ids), Hkv, D), qd)
+    vn = _rand_storage(gen, (len(ids), Hkv, D), qd)
+    pkv.pkv_reshape_and_cache(_to_device(kn, qd), _to_device(vn, qd), dk, dv,
+                              torch.from_numpy(s1).cuda(), ksc, vsc)
+    O.reshape_and_cache(kn, vn, qd, k, v, cache, s2, bs, ksc, vsc)
+    torch.cuda.synchronize()
+    assert np.array_equal(G.bits(G.np_storage(dk)), G.bits(k)), "K pool differs"
+    _, tables, blens = bm.export(np.arange(S, dtype=np.int64))
+    return dict(k=k, v=v, dk=dk, dv=dv, tables=tables, lens=blens, mb=mb, qd=qd, ksc=ksc,
+                vsc=vsc, bs=bs)
+
+
+def _prefill_case(cache, D, grp, lens, chunks, bs=16, Hkv=2, label=""):
+    gen = torch.Generator().manual_seed(1000 + 97 * cache + D + 7 * grp + bs)
+    b = _paged_batch(gen, cache, D, Hkv, lens, bs, seed=grp + D)
+    Hq = Hkv * grp
+    qstart = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    R = int(qstart[-1])
+    q = _rand_storage(gen, (R, Hq, D), b["qd"])
+    dq = _to_device(q, b["qd"])
+    out_t = torch.float32 if cache == F32 else torch.bfloat16
+    d_tables = torch.from_numpy(b["tables"]).cuda()
+    scale = 1 / math.sqrt(D)
+    p = pkv.make_prefill_params(dq, b["dk"], d_tables, len(lens), b["mb"] * bs, scale, b["ksc"],
+                                b["vsc"], out_t)
+    out = torch.full((R, Hq, D), float("nan"), dtype=out_t, device="cuda")
+    lse = torch.full((R, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    G.log(f"[prefill {label}] dtype={cache} D={D} G={grp} bs={bs} rows={R}")
+    pkv.pkv_prefill_attention(p, out, dq, b["dk"], b["dv"], d_tables,
+                              torch.from_numpy(b["lens"]).cuda(), torch.from_numpy(qstart).cuda(),
+                              lse)
+    torch.cuda.synchronize()
+    ref, rlse = O.prefill_attention(q, b["qd"], b["k"], b["v"], cache, b["tables"], b["lens"],
+                                    qstart, Hkv, bs, float(np.float32(scale)), b["ksc"], b["vsc"])
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    err = np.abs(got - ref)
+    if cache == F32:
+        bound = 1e-5 * np.abs(ref).max(axis=2, keepdims=True)
+        assert np.all(err <= np.maximum(bound, 1e-30)), f"{label}: fp32 err"
+    else:
+        assert err.max() <= G_TOL[cache], f"{label}: max abs err {err.max()}"
+    gl = lse.cpu().numpy()
+    fin = np.isfinite(rlse)
+    assert np.array_equal(fin, np.isfinite(gl)), f"{label}: lse finiteness"
+    assert np.allclose(gl[fin], rlse[fin], rtol=1e-4, atol=1e-4), f"{label}: lse"
+    return got, ref
+
+
+G_TOL = G.TOL
+PF_LENS = [1, 17, 100, 700, 2049, 3000]
+PF_CHUNKS = [1, 17, 37, 300, 1, 160]
+
+
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("group", [1, 3, 4, 8, 16])
+def test_prefill_mixed_chunks(cache, D, group):
+    _prefill_case(cache, D, group, PF_LENS, PF_CHUNKS, label=f"mixed")
+
+
+@pytest.mark.parametrize("cache", [BF16, E4M3])
+def test_prefill_block_size_32(cache):
+    _prefill_case(cache, 128, 4, PF_LENS, PF_CHUNKS, bs=32, label="bs32")
+
+
+def test_prefill_full_sequences_and_overlong_chunks():
+    """C = L (the whole sequence is the chunk) and C > L (leading rows see
+    nothing and are written as zeros with lse = -inf)."""
+    got, ref = _prefill_case(BF16, 128, 4, [1000, 3, 64], [1000, 5, 64], label="full/overlong")
+    assert np.all(got[1000:1002] == 0)
