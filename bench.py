@@ -47,6 +47,10 @@ def parse():
                     help="tokens per split-KV partition (-1: the workload's choice)")
     ap.add_argument("--block-size", type=int, default=16, choices=(16, 32),
                     help="tokens per physical KV block")
+    ap.add_argument("--op", default="decode", choices=("decode", "prefill"),
+                    help="decode step (default) or chunked-prefill attention")
+    ap.add_argument("--chunk", type=int, default=512,
+                    help="query tokens per sequence for --op prefill (the last ones of each context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=0,
                     help="sequences in the oracle sample (0: the default for the workload)")
@@ -135,6 +139,9 @@ def main():
 
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.op == "prefill":
+        prefill_bench(args)
         return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pkv.lib()
@@ -269,6 +276,76 @@ def main():
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(spec, w, bm, ids, args, pkv, torch)
+    print(json.dumps(res), flush=True)
+
+
+MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0, 2: 2500.0}  # fp32 MFMA; bf16 MFMA (fp8 KV is widened to bf16)
+
+
+def prefill_bench(args):
+    """Chunked-prefill attention: every sequence of the workload attends its
+    last `chunk` tokens causally over its whole paged context (K/V already in
+    the cache).  Roofline against the dense MFMA peak of the compute dtype:
+    algorithmic FLOPs = sum over query rows and heads of 4 * D * (p + 1)."""
+    import torch
+
+    import paged_kv_cache_189_amd as pkv
+    import workloads
+    dev = torch.device("cuda:0")
+    spec = dataclasses.replace(workloads.SPECS[args.config], block_size=args.block_size)
+    BS = spec.block_size
+    lens = workloads.lengths(spec)
+    S = len(lens)
+    w = workloads.make(spec, device=dev, lens=lens)
+    bm = pkv.BlockManager(w.num_blocks, BS, w.max_blocks, w.free_order)
+    workloads.allocate_context(bm, spec, lens)
+    ids = np.arange(S, dtype=np.int64)
+    _, tables, blens = bm.export(ids)
+    workloads.poison_unused(w, tables, blens)
+    chunks = np.minimum(blens, args.chunk).astype(np.int64)
+    qstart = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    R = int(qstart[-1])
+    gen = torch.Generator(device=dev).manual_seed(7000 + spec.index)
+    qdt = torch.float32 if spec.q_dtype == workloads.F32 else torch.bfloat16
+    q = torch.randn((R, spec.num_q_heads, spec.head_dim), generator=gen, device=dev).to(qdt)
+    out = torch.empty_like(q)
+    lse = torch.empty((R, spec.num_q_heads), dtype=torch.float32, device=dev)
+    d_tables = torch.from_numpy(tables).to(dev)
+    d_lens = torch.from_numpy(blens).to(dev)
+    d_qs = torch.from_numpy(qstart).to(dev)
+    p = pkv.make_prefill_params(q, w.k_cache, d_tables, S, w.max_blocks * BS, w.scale, w.k_scale,
+                                w.v_scale, qdt)
+    run = lambda: pkv.pkv_prefill_attention(p, out, q, w.k_cache, w.v_cache, d_tables, d_lens,
+                                            d_qs, lse)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    # causal work: row j of sequence s sees L_s - C_s + j + 1 tokens
+    seen = sum(int(c) * (int(L) - int(c)) + int(c) * (int(c) + 1) // 2 for L, c in zip(blens, chunks))
+    flops = 4.0 * spec.num_q_heads * spec.head_dim * seen
+    kvb, _ = kv_bytes(spec, tables, blens)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[spec.cache_dtype]
+    res = {"metric": "chunked prefill attention: TFLOP/s", "value": round(tflops, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 4), "higher_is_better": True, "vs_baseline": None,
+           "dtype": {0: "f32", 1: "bf16", 2: "fp8-e4m3 kv, bf16 q/out"}[spec.cache_dtype],
+           "data": "synthetic (seeded N(0,1) values, shuffled block tables)",
+           "config": {"workload": spec.name, "seqs": S, "query_tokens": R, "chunk": args.chunk,
+                      "block_size": BS, "parallelism": "1 GPU"},
+           "kv_bytes": int(kvb), "kv_gbs": round(kvb / (ms * 1e-3) / 1e9, 1),
+           "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tflops, 2),
+                        "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                        "traffic": None, "flops_per_launch": flops,
+                        "avg_launch_us": round(ms * 1e3, 2)}}
     print(json.dumps(res), flush=True)
 
 

@@ -1133,17 +1133,26 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 }
 
 // ---------------------------------------------------------------- chunked prefill
-// One wave per (kv head g, sequence s, query tile): a tile holds
-// tokens_per_tile = 16 / G query tokens of the chunk, row r = token r / G,
-// head r % G, so the G heads of a token share the K/V tile as in decode.
-// Row r's query token sits at position p = L - C + j of its sequence and sees
-// tokens 0..p (causal); the wave walks tiles up to its last row's position.
-// Rows past the chunk copy the tile's last row and are not written; rows
-// with p < 0 (chunk longer than the context) are written as zeros.
+// One wave per (kv head g, sequence s, group of NR query tiles).  A tile
+// holds tokens_per_tile = 16 / G query tokens of the chunk, row r = token
+// r / G, head r % G, so the G heads of a token share the K/V tile as in
+// decode; the NR tiles of a wave share every K/V fragment it loads (NR times
+// the MFMA work per byte).  Row r's query token sits at position p = L - C + j
+// of its sequence and sees tokens 0..p (causal); the wave walks tiles up to
+// its last row's position.  Rows past the chunk copy the group's last row and
+// are not written; rows with p < 0 (chunk longer than the context) are written
+// as zeros.
+template <int KIND, int D>
+struct PrefillRows {
+  static constexpr int NR = KIND == kF32 ? 1 : (D == 128 ? 2 : 4);  // row tiles per wave (register bound)
+  static constexpr int S = 2;                  // K/V register buffers
+};
+
 template <int KIND, int D, int S, int SH>
-__device__ __forceinline__ void prefill_tile(const PrefillArgs& a, QLds<KIND, D>& qs, int s, int g,
-                                             int qt) {
+__device__ __forceinline__ void prefill_group(const PrefillArgs& a, QLds<KIND, D>* qs, int s,
+                                              int g, int grp) {
   using T = Tile<KIND, D>;
+  constexpr int NR = PrefillRows<KIND, D>::NR;
   constexpr int NW = 1;
   constexpr int shift = SH;
   const int lane = threadIdx.x & 63;
@@ -1153,28 +1162,42 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, QLds<KIND, D>
   const int q0 = qst[s], C = qst[s + 1] - q0;
   int Ls = as_const(a.context_lens)[s];
   Ls = Ls < 0 ? 0 : (Ls > a.max_context_len ? a.max_context_len : Ls);
+  const int jbase = grp * NQ * NR;  // first chunk token of the group
+  const int jlast = (jbase + NQ * NR < C ? jbase + NQ * NR : C) - 1;
+  const int Lmax = Ls - C + jlast + 1;  // wave-uniform: tokens the group's last row sees
   const int jl = r / G, hh = r % G;
-  const int j = qt * NQ + jl;
-  const bool row_ok = r < NQ * G && j < C;
-  const int jlast = (qt * NQ + NQ < C ? qt * NQ + NQ : C) - 1;
-  const int jj = row_ok ? j : jlast;
-  const int Lrow = Ls - C + jj + 1;            // tokens this row sees (<= 0: none)
-  const int Lmax = Ls - C + jlast + 1;         // wave-uniform: the tile's last row
-  const int L = Lrow > 1 ? Lrow : 1;           // empty rows look at token 0, then write zeros
+  int L[NR];
+  bool row_ok[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    const int j = jbase + k * NQ + jl;
+    row_ok[k] = r < NQ * G && j < C;
+    const int Lrow = Ls - C + (row_ok[k] ? j : jlast) + 1;
+    L[k] = Lrow > 1 ? Lrow : 1;  // empty rows look at token 0, then write zeros
+  }
 
-  u32x4 qreg[T::NQ];
+  // Q^T fragments of the NR tiles, staged in this wave's LDS.  Lane l stages
+  // the fragment of lane l ^ 1, so every read below comes from another lane's
+  // write and stays an LDS read (the tiles do not fit in registers).
   {
     constexpr int QES = KIND == kF32 ? 4 : 2;
-    const gchar_p qrow = (gchar_p) static_cast<const char*>(a.q) +
-                         ((int64_t)(q0 + jj) * Hq + g * G + hh) * D * QES;
+    const int pl = lane ^ 1, pr = pl & 15, pq4 = pl >> 4;
+    const int pjl = pr / G, phh = pr % G;
 #pragma unroll
-    for (int jq = 0; jq < T::NQ; ++jq) {
-      int off;
-      if constexpr (KIND == kFP8)
-        off = ((jq >> 1) * 4 + q4) * 32 + (jq & 1) * 16;
-      else
-        off = (jq * 4 + q4) * 16;
-      qreg[jq] = *reinterpret_cast<gptr<u32x4>>(qrow + off);
+    for (int k = 0; k < NR; ++k) {
+      const int j = jbase + k * NQ + pjl;
+      const int jj = pr < NQ * G && j < C ? j : jlast;
+      const gchar_p qrow = (gchar_p) static_cast<const char*>(a.q) +
+                           ((int64_t)(q0 + jj) * Hq + g * G + phh) * D * QES;
+#pragma unroll
+      for (int jq = 0; jq < T::NQ; ++jq) {
+        int off;
+        if constexpr (KIND == kFP8)
+          off = ((jq >> 1) * 4 + pq4) * 32 + (jq & 1) * 16;
+        else
+          off = (jq * 4 + pq4) * 16;
+        qs[k].qf[jq][pl] = *reinterpret_cast<gptr<u32x4>>(qrow + off);
+      }
     }
   }
 
@@ -1192,8 +1215,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, QLds<KIND, D>
     vt = uniform_ptr(vbase + phys * bstride + half * (kBS * T::ES));
   };
 
-  RunState<KIND, D> st;
-  st.init();
+  RunState<KIND, D> st[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) st[k].init();
   const int b_end = Lmax > 0 ? (Lmax + kBS - 1) / kBS : 0;
   int b = 0;
   if (b < b_end) {
@@ -1202,16 +1226,17 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, QLds<KIND, D>
 #define PKV_PREFETCH(BUF, AHEAD)                          \
   tile_of(min(b + (AHEAD)*NW, b_end - 1), kt, vt);        \
   load_tile<KIND, D, SH == 0>(BUF, kt, vt, toff);
-#define PKV_STAGE(CUR, NXT)                                                     \
-  PKV_PREFETCH(NXT, S - 1)                                                      \
-  process_block<KIND, D>(st, CUR, qs, b, L, Lmax, a.score_scale_log2, lane, q4); \
-  b += NW;                                                                      \
+#define PKV_STAGE(CUR, NXT)                                                               \
+  PKV_PREFETCH(NXT, S - 1)                                                                \
+  _Pragma("unroll") for (int k = 0; k < NR; ++k) {                                        \
+    process_block<KIND, D>(st[k], CUR, qs[k], b, L[k], Lmax, a.score_scale_log2, lane, q4); \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+  }                                                                                       \
+  b += NW;                                                                                \
   if (b >= b_end) break;
     PKV_PREFETCH(f0, 0)
     if constexpr (S >= 3) { PKV_PREFETCH(f1, 1) }
     if constexpr (S >= 4) { PKV_PREFETCH(f2, 2) }
-#pragma unroll
-    for (int jq = 0; jq < T::NQ; ++jq) qs.qf[jq][lane] = qreg[jq];
     if constexpr (S == 2) {
       for (;;) { PKV_STAGE(f0, f1) PKV_STAGE(f1, f0) }
     } else if constexpr (S == 3) {
@@ -1222,41 +1247,47 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, QLds<KIND, D>
 #undef PKV_STAGE
 #undef PKV_PREFETCH
   }
-  const float l_run = sum_across_groups(st.l);
-  const float e_run = sum_across_groups(st.e);
-  if (!row_ok) return;
-  const bool empty = Lrow <= 0;
-  const int64_t row = (int64_t)(q0 + j) * Hq + g * G + hh;
-  const float inv = !empty && l_run > 0.f ? a.v_scale / l_run : 0.f;
 #pragma unroll
-  for (int nt = 0; nt < T::NT; ++nt) {
-    const int d = nt * 16 + 4 * q4;
-    const f32x4 o = st.acc.o[nt] * inv;
-    if constexpr (KIND == kF32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d) = o;
-    } else {
-      const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * D + d) = u32x2{lo, hi};
+  for (int k = 0; k < NR; ++k) {
+    const float l_run = sum_across_groups(st[k].l);
+    const float e_run = sum_across_groups(st[k].e);
+    if (!row_ok[k]) continue;
+    const int j = jbase + k * NQ + jl;
+    const bool empty = Ls - C + j + 1 <= 0;
+    const int64_t row = (int64_t)(q0 + j) * Hq + g * G + hh;
+    const float inv = !empty && l_run > 0.f ? a.v_scale / l_run : 0.f;
+#pragma unroll
+    for (int nt = 0; nt < T::NT; ++nt) {
+      const int d = nt * 16 + 4 * q4;
+      const f32x4 o = st[k].acc.o[nt] * inv;
+      if constexpr (KIND == kF32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d) = o;
+      } else {
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * D + d) = u32x2{lo, hi};
+      }
     }
+    if (q4 == 0 && a.lse)
+      a.lse[row] = !empty && e_run > 0.f ? (st[k].m + __builtin_amdgcn_logf(e_run)) * kLn2 : -INFINITY;
   }
-  if (q4 == 0 && a.lse)
-    a.lse[row] = !empty && e_run > 0.f ? (st.m + __builtin_amdgcn_logf(e_run)) * kLn2 : -INFINITY;
 }
 
-// Items (g, s, tile) lie head major: item g * TQ + ct[s] + tile, ct = prefix
-// sums of the sequences' tile counts, built in LDS by every workgroup.
-// Workgroup b takes items ((b mod 8) * (nWG / 8) + b / 8) * NW + w, so one XCD
-// works through consecutive tiles of the same sequences and shares their K/V
-// tiles in its L2.
+// Items (g, s, group) lie head major: item g * TQ + ct[s] + group, ct =
+// prefix sums of the sequences' group counts, built in LDS by every
+// workgroup.  Workgroup b takes items ((b mod 8) * (nWG / 8) + b / 8) * NW + w,
+// so one XCD works through consecutive groups of the same sequences and
+// shares their K/V tiles in its L2.
 template <int KIND, int D, int NW, int S, int SH>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
-  __shared__ QLds<KIND, D> qs[NW];
+  constexpr int NR = PrefillRows<KIND, D>::NR;
+  __shared__ QLds<KIND, D> qs[NW][NR];
   __shared__ int lct[kPrefillMaxSeqs + 1];
   __shared__ int wsums[NW];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nseq = a.num_seqs, H = a.num_kv_heads, NQ = a.tokens_per_tile;
+  const int nseq = a.num_seqs, H = a.num_kv_heads;
+  const int per = a.tokens_per_tile * NR;  // query tokens per item
   {
     const int tid = threadIdx.x;
     int carry = 0;
@@ -1265,7 +1296,7 @@ void prefill_kernel(PrefillArgs a) {
       int C = s < nseq ? a.query_start[s + 1] - a.query_start[s] : 0;
       C = C < 0 ? 0 : C;
       int tot;
-      const int e = block_exclusive_scan<NW>((C + NQ - 1) / NQ, wsums, &tot);
+      const int e = block_exclusive_scan<NW>((C + per - 1) / per, wsums, &tot);
       if (s < nseq) lct[s] = carry + e;
       carry += tot;
     }
@@ -1282,7 +1313,7 @@ void prefill_kernel(PrefillArgs a) {
     const int mid = (lo + hi) >> 1;
     if (lct[mid] <= rem) lo = mid; else hi = mid;
   }
-  prefill_tile<KIND, D, S, SH>(a, qs[w], lo, g, rem - lct[lo]);
+  prefill_group<KIND, D, S, SH>(a, qs[w], lo, g, rem - lct[lo]);
 }
 
 // Register buffers (prefetch depth + 1) per cache dtype, at two waves per
@@ -1435,8 +1466,10 @@ hipError_t launch_prefill(const PrefillArgs& a, int cache, int D, int64_t num_ro
                           hipStream_t stream, bool* supported) {
   *supported = true;
   if (a.num_seqs == 0 || num_rows == 0) return hipSuccess;
-  // waves: at most one per query tile, tiles <= rows / tokens_per_tile + one partial per sequence
-  const int64_t tiles = (num_rows + a.tokens_per_tile - 1) / a.tokens_per_tile + a.num_seqs;
+  // waves: at most one per group of NR query tiles; groups <= rows / tokens
+  // per group + one partial group per sequence
+  const int per = a.tokens_per_tile * (cache == kF32 ? 1 : (D == 128 ? 2 : 4));
+  const int64_t tiles = (num_rows + per - 1) / per + a.num_seqs;
   int64_t groups = ((int64_t)a.num_kv_heads * tiles + kWavesPerGroup - 1) / kWavesPerGroup;
   groups = (groups + 7) / 8 * 8;
   if (groups > INT32_MAX) {
@@ -1446,7 +1479,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int cache, int D, int64_t num_ro
   const dim3 grid((unsigned)groups), block(kWavesPerGroup * 64);
 #define PKV_PF(C_, D_, SH_)                                                                   \
   if (cache == C_ && D == D_ && a.block_shift == SH_) {                                       \
-    hipLaunchKernelGGL((prefill_kernel<C_, D_, kWavesPerGroup, Depth<C_>::value, SH_>), grid, \
+    hipLaunchKernelGGL((prefill_kernel<C_, D_, kWavesPerGroup, PrefillRows<C_, D_>::S, SH_>), grid, \
                        block, 0, stream, a);                                                  \
     return hipGetLastError();                                                                 \
   }
