@@ -117,6 +117,43 @@ pkv_status pkv_bm_append_slots_cow(pkv_block_manager* bm, const int64_t* seq_ids
                                    int64_t* slot_mapping_out, int32_t* copy_src_out,
                                    int32_t* copy_dst_out, int32_t* num_copies_out);
 
+/* ---- Automatic prefix caching ------------------------------------------
+ * ([P1] and [P3] turn it on with an engine flag and credit it for the
+ * highest of the pages' throughput figures; they describe no scheme, so the
+ * following is this library's reading.)  A full block of a sequence whose
+ * token ids are known is registered under its content: its block_size ids
+ * and its parent, the registered block of the previous logical block.  A new
+ * prompt walks its full blocks from the start and reuses each registered
+ * block whose whole token prefix equals the prompt's, so its K and V need
+ * not be computed again.  A registered block whose reference count drops to
+ * 0 stays cached: allocation takes the free queue first, then evicts the
+ * least recently released cached block, which also drops its cached
+ * descendants (they join the free queue after it, depth first).
+ * pkv_bm_num_free_blocks counts cached unreferenced blocks as free. */
+
+/* Adds sequence seq_id with the n prompt tokens token_ids (host).  Reuses
+ * cached blocks for the longest matching prefix of full blocks, at most
+ * (n - 1) / block_size of them (the last prompt token is always computed),
+ * takes fresh blocks for the rest, and writes the slots of all n tokens to
+ * slot_mapping_out (host, n entries).  *num_cached_out = tokens at the start
+ * of the prompt whose K and V are already in the cache (a multiple of
+ * block_size); the caller writes K and V only for the tokens after them.
+ * Full blocks the prompt fills are registered.  Errors: SEQ_EXISTS,
+ * INVALID_ARG (outgrows max_blocks_per_seq), OUT_OF_BLOCKS (nothing
+ * changes). */
+pkv_status pkv_bm_add_seq_prompt(pkv_block_manager* bm, int64_t seq_id, const int32_t* token_ids,
+                                 int32_t n, int64_t* slot_mapping_out, int32_t* num_cached_out);
+
+/* pkv_bm_append_slots with the appended tokens' ids (token_ids, host, n
+ * entries): a block of a sequence added by pkv_bm_add_seq_prompt (or forked
+ * from one) that becomes full is registered.  A sequence that receives a
+ * token through an id-less call stops being registered from then on. */
+pkv_status pkv_bm_append_tokens(pkv_block_manager* bm, const int64_t* seq_ids,
+                                const int32_t* token_ids, int32_t n, int64_t* slot_mapping_out);
+
+/* Registered blocks (referenced or waiting in the LRU list). */
+int32_t pkv_bm_num_cached_blocks(const pkv_block_manager* bm);
+
 /* Drops the sequence; each of its blocks loses one reference ([P4] §4). */
 pkv_status pkv_bm_free_seq(pkv_block_manager* bm, int64_t seq_id);
 

@@ -33,7 +33,8 @@ PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
 # every symbol include/pkv.h declares
 EXPORTED = (
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_seq", "pkv_bm_fork_seq",
-    "pkv_bm_append_slots", "pkv_bm_append_slots_cow", "pkv_bm_free_seq", "pkv_bm_export",
+    "pkv_bm_append_slots", "pkv_bm_append_slots_cow", "pkv_bm_add_seq_prompt",
+    "pkv_bm_append_tokens", "pkv_bm_num_cached_blocks", "pkv_bm_free_seq", "pkv_bm_export",
     "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_reshape_and_cache", "pkv_copy_blocks",
     "pkv_decode_workspace_bytes",
     "pkv_decode_partition_size", "pkv_decode_attention", "pkv_decode_attention_partitions",
@@ -93,6 +94,9 @@ def lib():
             "pkv_bm_fork_seq": (st, [P, I64, I64]),
             "pkv_bm_append_slots": (st, [P, P, I32, P]),
             "pkv_bm_append_slots_cow": (st, [P, P, I32, P, P, P, P]),
+            "pkv_bm_add_seq_prompt": (st, [P, I64, P, I32, P, P]),
+            "pkv_bm_append_tokens": (st, [P, P, P, I32, P]),
+            "pkv_bm_num_cached_blocks": (I32, [P]),
             "pkv_bm_free_seq": (st, [P, I64]),
             "pkv_bm_export": (st, [P, P, I32, P, P]),
             "pkv_bm_num_free_blocks": (I32, [P]),
@@ -214,6 +218,28 @@ class BlockManager:
                                            src.ctypes.data, dst.ctypes.data, C.byref(n))
         k = n.value if rc == PKV_OK else 0
         return rc, slots, src[:k].copy(), dst[:k].copy()
+
+    def add_seq_prompt(self, seq_id: int, token_ids):
+        """Returns (status, slots of every prompt token, number of cached tokens)."""
+        ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+        slots = np.empty(max(ids.size, 1), dtype=np.int64)
+        n = C.c_int32(0)
+        rc = lib().pkv_bm_add_seq_prompt(self.h, seq_id, ids.ctypes.data, ids.size,
+                                         slots.ctypes.data, C.byref(n))
+        return rc, slots[:ids.size].copy(), n.value
+
+    def append_tokens(self, seq_ids, token_ids, out: Optional[np.ndarray] = None):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tok = np.ascontiguousarray(token_ids, dtype=np.int32)
+        if tok.shape != ids.shape:
+            raise ValueError("one token id per appended token")
+        slots = out if out is not None else np.empty(ids.shape, dtype=np.int64)
+        rc = lib().pkv_bm_append_tokens(self.h, ids.ctypes.data, tok.ctypes.data, ids.size,
+                                        slots.ctypes.data)
+        return rc, slots
+
+    def num_cached(self) -> int:
+        return lib().pkv_bm_num_cached_blocks(self.h)
 
     def free_seq(self, seq_id: int) -> int:
         return lib().pkv_bm_free_seq(self.h, seq_id)

@@ -534,3 +534,69 @@ def test_prefill_full_sequences_and_overlong_chunks():
     nothing and are written as zeros with lse = -inf)."""
     got, ref = _prefill_case(BF16, 128, 4, [1000, 3, 64], [1000, 5, 64], label="full/overlong")
     assert np.all(got[1000:1002] == 0)
+
+
+# ------------------------------------------------------------------- automatic prefix caching
+def test_prefix_cache_reuses_cached_kv_end_to_end():
+    """K and V are a fixed function of (token id, position), as a model's
+    would be of the token prefix.  Sequence A writes its prompt; after A is
+    freed, B shares A's first 40 tokens and C repeats A's prompt: they get
+    A's cached blocks back and write only their remaining tokens.  Tables
+    equal the oracle allocator's, and decode of B and C over the reused
+    blocks equals the oracle over pools where every token was written."""
+    from oracle.prefix_cache import PrefixCacheAllocator
+    gen = torch.Generator().manual_seed(4242)
+    Hq, Hkv, D, bs, nb, mb = 16, 4, 128, 16, 64, 16
+    vocab, maxpos = 60, mb * bs
+    kv_k = _rand_storage(gen, (vocab, maxpos, Hkv, D), BF16)   # K of token id at position
+    kv_v = _rand_storage(gen, (vocab, maxpos, Hkv, D), BF16)
+    order = np.random.default_rng(5).permutation(nb).astype(np.int32)
+    bm = pkv.BlockManager(nb, bs, mb, order)
+    ob = PrefixCacheAllocator(nb, bs, mb, order)
+    ks, vs = workloads.pool_shapes(nb, Hkv, D, BF16, bs)
+    k_all = np.zeros(ks, np.uint16)   # oracle pools: every token written
+    v_all = np.zeros(vs, np.uint16)
+    dk, dv = _to_device(k_all.copy(), BF16), _to_device(v_all.copy(), BF16)
+    rng = np.random.default_rng(6)
+    prompt_a = list(rng.integers(0, vocab, 70))
+    prompts = {0: prompt_a, 1: prompt_a[:40] + list(rng.integers(0, vocab, 30)), 2: list(prompt_a)}
+
+    def admit(sid):
+        toks = prompts[sid]
+        r1, s1, c1 = bm.add_seq_prompt(sid, toks)
+        r2, s2, c2 = ob.add_seq_prompt(sid, toks)
+        assert r1 == r2 == 0 and list(s1) == s2 and c1 == c2
+        pos = np.arange(len(toks))
+        tk = np.asarray(toks)
+        kn, vn = kv_k[tk, pos], kv_v[tk, pos]
+        new = slice(c1, len(toks))   # the device gets only the tokens not cached
+        pkv.pkv_reshape_and_cache(_to_device(np.ascontiguousarray(kn[new]), BF16),
+                                  _to_device(np.ascontiguousarray(vn[new]), BF16), dk, dv,
+                                  torch.from_numpy(np.ascontiguousarray(s1[new])).cuda())
+        O.reshape_and_cache(np.ascontiguousarray(kn), np.ascontiguousarray(vn), BF16, k_all,
+                            v_all, BF16, np.asarray(s1, np.int64), bs)
+        return c1
+
+    G.log("[prefix cache] admit A, free it, admit B and C")
+    assert admit(0) == 0
+    assert bm.free_seq(0) == ob.free_seq(0) == 0
+    assert admit(1) == 32            # two full blocks of the shared 40 tokens
+    assert admit(2) == 64            # four full blocks; the fifth holds the last token
+    seqs = np.array([1, 2], dtype=np.int64)
+    _, tables, lens = bm.export(seqs)
+    for i, sid in enumerate(seqs):
+        t, L = ob.table(int(sid))
+        assert list(tables[i][: len(t)]) == t and lens[i] == L
+    q = _rand_storage(gen, (2, Hq, D), BF16)
+    dq = _to_device(q, BF16)
+    d_tables = torch.from_numpy(tables).cuda()
+    params = pkv.make_decode_params(dq, dk, d_tables, mb * bs, 1 / math.sqrt(D), 1.0, 1.0,
+                                    torch.bfloat16, 0)
+    ws = torch.empty(pkv.pkv_decode_workspace_bytes(params), dtype=torch.uint8, device="cuda")
+    out = torch.empty((2, Hq, D), dtype=torch.bfloat16, device="cuda")
+    pkv.pkv_decode_attention(params, out, dq, dk, dv, d_tables, torch.from_numpy(lens).cuda(), ws)
+    torch.cuda.synchronize()
+    ref, _ = O.decode_attention(q, BF16, k_all, v_all, BF16, tables, lens, Hkv, bs,
+                                float(np.float32(1 / math.sqrt(D))))
+    err = np.abs(out.float().cpu().numpy() - ref).max()
+    assert err <= G.TOL[BF16], err
