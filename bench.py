@@ -47,8 +47,9 @@ def parse():
                     help="tokens per split-KV partition (-1: the workload's choice)")
     ap.add_argument("--block-size", type=int, default=16, choices=(16, 32),
                     help="tokens per physical KV block")
-    ap.add_argument("--op", default="decode", choices=("decode", "prefill"),
-                    help="decode step (default) or chunked-prefill attention")
+    ap.add_argument("--op", default="decode", choices=("decode", "prefill", "sim"),
+                    help="decode step (default), chunked-prefill attention, or the host-only "
+                         "continuous-batching simulation")
     ap.add_argument("--chunk", type=int, default=512,
                     help="query tokens per sequence for --op prefill (the last ones of each context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -139,6 +140,9 @@ def main():
 
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.op == "sim":
+        sim_bench(args)
         return
     if args.op == "prefill":
         prefill_bench(args)
@@ -280,6 +284,54 @@ def main():
 
 
 MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0, 2: 2500.0}  # fp32 MFMA; bf16 MFMA (fp8 KV is widened to bf16)
+
+
+def sim_bench(args):
+    """Host-only: the block manager under continuous batching on a synthetic
+    request trace, paging versus a static reservation of max_model_len, and
+    paging with the prefix cache.  Shape: Llama-3-8B on a 40 GB GPU with 90%
+    of its memory for the engine (16 GB of weights, 128 KiB of KV per token),
+    max-model-len 8192, max-num-seqs 256, 16-token blocks; 2000 requests with
+    log-normal prompt (median 600) and output (median 250) lengths, 60% of
+    them opening with one of four 512-token system prompts."""
+    import paged_kv_cache_189_amd as pkv
+    rng = np.random.default_rng(2024)
+    R, BS, ML, MNS = 2000, 16, 8192, 256
+    kv_per_token = 2 * 32 * 8 * 128 * 2
+    nb = int((40e9 * 0.90 - 16.06e9) // (kv_per_token * BS))
+    systems = [list(rng.integers(0, 32000, 512)) for _ in range(4)]
+    prompts, outs = [], []
+    for r in range(R):
+        n = int(np.clip(np.rint(rng.lognormal(np.log(600), 0.8)), 1, 6000))
+        o = int(np.clip(np.rint(rng.lognormal(np.log(250), 0.8)), 1, 2000))
+        p = list(rng.integers(0, 32000, n))
+        if rng.random() < 0.6:
+            p = systems[int(rng.integers(0, 4))] + p
+        prompts.append(p[: ML - o])
+        outs.append(o)
+    pl = np.array([len(p) for p in prompts], dtype=np.int32)
+    ol = np.array(outs, dtype=np.int32)
+    ids = np.concatenate(prompts).astype(np.int32)
+    runs = {}
+    for name, pol, cache in (("static_reservation", pkv.PKV_SIM_STATIC, False),
+                             ("paged", pkv.PKV_SIM_PAGED, False),
+                             ("paged_prefix_cache", pkv.PKV_SIM_PAGED, True)):
+        t0 = time.perf_counter()
+        rc, res, _ = pkv.pkv_sim_run(nb, BS, ML, MNS, pol, pl, ol, ids, cache)
+        secs = time.perf_counter() - t0
+        assert rc == pkv.PKV_OK, pkv.lib().pkv_last_error().decode()
+        res["tokens_per_iteration"] = round(res["generated_tokens"] / res["iterations"], 2)
+        res["host_us_per_iteration"] = round(secs * 1e6 / res["iterations"], 2)
+        res["mean_running"] = round(res["mean_running"], 2)
+        res["mean_kv_utilization"] = round(res["mean_kv_utilization"], 4)
+        runs[name] = res
+    ratio = runs["paged"]["tokens_per_iteration"] / runs["static_reservation"]["tokens_per_iteration"]
+    print(json.dumps({"metric": "continuous-batching simulation: generated tokens per iteration",
+                      "value": runs["paged"]["tokens_per_iteration"], "unit": "tokens/iteration",
+                      "higher_is_better": True, "data": "synthetic request trace (seeded)",
+                      "config": {"requests": R, "num_blocks": nb, "block_size": BS,
+                                 "max_model_len": ML, "max_num_seqs": MNS},
+                      "paged_over_static": round(ratio, 3), "runs": runs}), flush=True)
 
 
 def prefill_bench(args):

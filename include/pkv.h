@@ -349,6 +349,59 @@ pkv_status pkv_prefill_attention(const pkv_prefill_params* p, void* out, const v
                                  const int32_t* query_start, float* lse_out, void* stream);
 
 /* ======================================================================== */
+/* Continuous-batching simulation (host only)                                */
+/* ======================================================================== */
+/* Runs a request trace through a scheduler over the block manager and
+ * reports concurrency and KV-memory use, comparing paging with a static
+ * per-request reservation of max_model_len ([P2] on continuous batching and
+ * max-num-seqs; [P4] §2 on the waste of static reservation).  Scheduler
+ * (this library's reading), per iteration:
+ *  1. admission in queue order while fewer than max_num_seqs run: PAGED adds
+ *     the request's tokens so far as one prompt (through the prefix cache
+ *     when prefix_cache != 0), STATIC reserves ceil(max_model_len /
+ *     block_size) blocks; the first request that does not fit stops it;
+ *  2. every running request, in admission order, appends one token; when the
+ *     pool is full the most recently admitted running request is preempted
+ *     (blocks freed, back to the front of the queue, its tokens recomputed on
+ *     re-admission) and the append is retried; a request reaching its output
+ *     length is freed at once;
+ *  3. statistics after the step.
+ * Generated token t of request r has id (r * 7919 + t) % 32000. */
+enum { PKV_SIM_PAGED = 0, PKV_SIM_STATIC = 1 };
+
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t max_model_len;  /* prompt + output of every request must fit */
+  int32_t max_num_seqs;
+  int32_t policy;         /* PKV_SIM_PAGED or PKV_SIM_STATIC */
+  int32_t prefix_cache;   /* PAGED only: admit prompts through the prefix cache */
+} pkv_sim_config;
+
+typedef struct {
+  int64_t iterations;         /* decode steps until every request finished */
+  int64_t generated_tokens;   /* tokens appended (recomputed ones excluded) */
+  int64_t preemptions;
+  int64_t peak_running;
+  double mean_running;        /* running requests per iteration */
+  double mean_kv_utilization; /* tokens held (per sequence) / slots of the blocks in use;
+                                 above 1 when sequences share blocks */
+  int64_t admitted_tokens;    /* tokens added at admissions (prompts, recomputations) */
+  int64_t cached_tokens;      /* of those, found in the prefix cache */
+} pkv_sim_result;
+
+/* prompt_lens, output_lens: num_requests entries (host), each > 0 and
+ * prompt + output <= max_model_len and fitting the pool.  prompt_ids: NULL
+ * or the prompts' token ids concatenated (required with prefix_cache).
+ * running_per_iter: NULL or max_iters entries receiving the running count
+ * after each iteration.  INVALID_ARG when a request cannot fit or max_iters
+ * is reached. */
+pkv_status pkv_sim_run(const pkv_sim_config* cfg, const int32_t* prompt_lens,
+                       const int32_t* output_lens, const int32_t* prompt_ids,
+                       int32_t num_requests, pkv_sim_result* out, int32_t* running_per_iter,
+                       int64_t max_iters);
+
+/* ======================================================================== */
 /* Diagnostics                                                               */
 /* ======================================================================== */
 const char* pkv_status_string(pkv_status s);

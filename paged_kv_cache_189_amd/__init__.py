@@ -38,7 +38,7 @@ EXPORTED = (
     "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_reshape_and_cache", "pkv_copy_blocks",
     "pkv_decode_workspace_bytes",
     "pkv_decode_partition_size", "pkv_decode_attention", "pkv_decode_attention_partitions",
-    "pkv_decode_attention_merge", "pkv_prefill_attention", "pkv_status_string",
+    "pkv_decode_attention_merge", "pkv_prefill_attention", "pkv_sim_run", "pkv_status_string",
     "pkv_last_error", "pkv_version",
 )
 
@@ -73,6 +73,21 @@ class pkv_prefill_params(C.Structure):
         ("q_dtype", C.c_int32), ("cache_dtype", C.c_int32), ("out_dtype", C.c_int32),
     ]
 
+
+class pkv_sim_config(C.Structure):
+    _fields_ = [("num_blocks", C.c_int32), ("block_size", C.c_int32),
+                ("max_model_len", C.c_int32), ("max_num_seqs", C.c_int32),
+                ("policy", C.c_int32), ("prefix_cache", C.c_int32)]
+
+
+class pkv_sim_result(C.Structure):
+    _fields_ = [("iterations", C.c_int64), ("generated_tokens", C.c_int64),
+                ("preemptions", C.c_int64), ("peak_running", C.c_int64),
+                ("mean_running", C.c_double), ("mean_kv_utilization", C.c_double),
+                ("admitted_tokens", C.c_int64), ("cached_tokens", C.c_int64)]
+
+
+PKV_SIM_PAGED, PKV_SIM_STATIC = 0, 1
 
 _lib = None
 
@@ -113,6 +128,8 @@ def lib():
                                                 P, P]),
             "pkv_prefill_attention": (st, [C.POINTER(pkv_prefill_params), P, P, P, P, P, P, P,
                                            P, P]),
+            "pkv_sim_run": (st, [C.POINTER(pkv_sim_config), P, P, P, I32,
+                                 C.POINTER(pkv_sim_result), P, I64]),
             "pkv_status_string": (C.c_char_p, [st]),
             "pkv_last_error": (C.c_char_p, []),
             "pkv_version": (C.c_char_p, []),
@@ -379,3 +396,24 @@ def pkv_prefill_attention(params: pkv_prefill_params, out: torch.Tensor, q: torc
         C.byref(params), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), _ptr(query_start), _ptr(lse), _stream(stream, out)),
         "pkv_prefill_attention")
+
+
+# ------------------------------------------------------------------ batching simulation
+def pkv_sim_run(num_blocks, block_size, max_model_len, max_num_seqs, policy, prompt_lens,
+                output_lens, prompt_ids=None, prefix_cache=False, max_iters=1 << 22,
+                want_trace=False):
+    """Returns (status, result dict, running count per iteration or None)."""
+    cfg = pkv_sim_config(num_blocks, block_size, max_model_len, max_num_seqs, policy,
+                         1 if prefix_cache else 0)
+    pl = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+    ol = np.ascontiguousarray(output_lens, dtype=np.int32)
+    ids = None if prompt_ids is None else np.ascontiguousarray(prompt_ids, dtype=np.int32)
+    res = pkv_sim_result()
+    trace = np.zeros(max_iters, dtype=np.int32) if want_trace else None
+    rc = lib().pkv_sim_run(C.byref(cfg), pl.ctypes.data, ol.ctypes.data,
+                           None if ids is None else ids.ctypes.data, pl.size, C.byref(res),
+                           None if trace is None else trace.ctypes.data, max_iters)
+    out = {name: getattr(res, name) for name, _ in pkv_sim_result._fields_}
+    if trace is not None and rc == PKV_OK:
+        trace = trace[: res.iterations].copy()
+    return rc, out, trace

@@ -52,9 +52,10 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
         cobj = os.path.join(tmp, "capi.o")
         run([hipcc, "-x", "hip", *HIP_FLAGS, "-c", os.path.join(CSRC, "capi.cpp"), "-o", cobj])
         objs.append(cobj)
-        bobj = os.path.join(tmp, "block_manager.o")
-        run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "block_manager.cpp"), "-o", bobj])
-        objs.append(bobj)
+        for name in ("block_manager", "sim"):
+            obj = os.path.join(tmp, name + ".o")
+            run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, name + ".cpp"), "-o", obj])
+            objs.append(obj)
         out_tmp = out + ".tmp"
         run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out_tmp])
         os.replace(out_tmp, out)
