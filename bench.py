@@ -178,42 +178,66 @@ def main():
     workloads.poison_unused(w, tables0[:, : w.max_blocks], lens0 - 1)
 
     out_dtype = torch.float32 if spec.out_dtype == workloads.F32 else torch.bfloat16
-    d_tables = torch.empty((S, max_blocks), dtype=torch.int32, device=dev)
-    d_lens = torch.empty(S, dtype=torch.int32, device=dev)
-    d_slots = torch.empty(S, dtype=torch.int64, device=dev)
+    # Device block tables are copied once; afterwards a step sends its slots,
+    # lengths and the table entries that changed (a sequence starting a new
+    # block) in one small packed buffer, and the entries are scattered on the
+    # device.
+    d_tables = torch.from_numpy(tables0).to(dev)
+    meta_bytes = 8 * S + 4 * S + 8 * S + 4 * S
+
+    def views(buf):
+        o = 0
+        out = []
+        for n, dt in ((8 * S, torch.int64), (4 * S, torch.int32), (8 * S, torch.int64),
+                      (4 * S, torch.int32)):
+            out.append(buf[o:o + n].view(dt))
+            o += n
+        return out
+
+    d_meta = torch.empty(meta_bytes, dtype=torch.uint8, device=dev)
+    d_slots, d_lens, d_upd_idx, d_upd_val = views(d_meta)
     params = pkv.make_decode_params(w.q, w.k_cache, d_tables, max_blocks * BS, w.scale, w.k_scale,
                                     w.v_scale, out_dtype, part)
     ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(params), 256), dtype=torch.uint8, device=dev)
     out = torch.empty(w.q.shape, dtype=out_dtype, device=dev)
     lse = torch.empty((S, spec.num_q_heads), dtype=torch.float32, device=dev)
-    # two pinned host buffer sets for the per-step metadata
-    pin = [dict(slots=torch.empty(S, dtype=torch.int64, pin_memory=True),
-                tables=torch.empty((S, max_blocks), dtype=torch.int32, pin_memory=True),
-                lens=torch.empty(S, dtype=torch.int32, pin_memory=True)) for _ in range(2)]
+    # two pinned host buffers for the per-step metadata
+    pin = []
+    for _ in range(2):
+        hb = torch.empty(meta_bytes, dtype=torch.uint8, pin_memory=True)
+        hs, hl, hi, hv = views(hb)
+        pin.append(dict(raw=hb, slots=hs, lens=hl, upd_idx=hi, upd_val=hv))
+    host_lens = blens.astype(np.int32).copy()
     copied = [torch.cuda.Event(), torch.cuda.Event()]
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
     build_s = time.perf_counter() - t_build
 
-    first = {"slots": slots0, "tables": tables0, "lens": blens}
-    lens_per_step, tables_last = [], None
+    lens_per_step = []
     ev = []
 
     def step(i, timed):
-        nonlocal tables_last
         buf = pin[i % 2]
         copied[i % 2].synchronize()  # the copy that last read this buffer is done
-        sl, tb, ln = buf["slots"].numpy(), buf["tables"].numpy(), buf["lens"].numpy()
+        sl, ln = buf["slots"].numpy(), buf["lens"].numpy()
+        n_upd = 0
         if i == 0:
-            sl[:], tb[:], ln[:] = first["slots"], first["tables"], first["lens"]
+            sl[:], ln[:] = slots0, host_lens
         else:
             rc, _ = bm.append_slots(ids, out=sl)                       # a1
             assert rc == 0, rc
-            bm.export(ids, tables=tb, lens=ln)
-        d_slots.copy_(buf["slots"], non_blocking=True)
-        d_tables.copy_(buf["tables"], non_blocking=True)
-        d_lens.copy_(buf["lens"], non_blocking=True)
+            pos = host_lens                       # position of each new token
+            new = np.nonzero(pos % BS == 0)[0]    # sequences that took a block
+            n_upd = len(new)
+            if n_upd:
+                buf["upd_idx"].numpy()[:n_upd] = new * max_blocks + pos[new] // BS
+                buf["upd_val"].numpy()[:n_upd] = sl[new] // BS
+            host_lens[:] = pos + 1
+            ln[:] = host_lens
+        d_meta.copy_(buf["raw"], non_blocking=True)
         copied[i % 2].record(stream)
+        if n_upd:
+            d_tables.view(-1).index_put_((d_upd_idx[:n_upd],), d_upd_val[:n_upd])
         pkv.pkv_reshape_and_cache(w.k_new, w.v_new, w.k_cache, w.v_cache, d_slots,  # a2
                                   w.k_scale, w.v_scale)
         if timed:
@@ -225,7 +249,6 @@ def main():
             e1.record(stream)
             ev.append((e0, e1))
             lens_per_step.append(ln.copy())
-            tables_last = tb
         pkv.pkv_decode_attention_merge(params, out, d_lens, ws, lse)             # a7
 
     for i in range(args.warmup):
@@ -241,7 +264,10 @@ def main():
     pass1_avg_ms = float(np.mean(pass1_ms))
 
     # algorithmic bytes, step by step (contexts grow by one token per step)
-    _, tables_now, _ = bm.export(ids)
+    _, tables_now, lens_now = bm.export(ids)
+    # the device tables kept by scattered updates must equal the manager's
+    assert np.array_equal(d_tables.cpu().numpy(), tables_now), "device block tables drifted"
+    assert np.array_equal(lens_now, host_lens), "context lengths drifted"
     kv_u, kv_l, oth = [], [], []
     for ln in lens_per_step:
         u, l = kv_bytes(spec, tables_now, ln)
