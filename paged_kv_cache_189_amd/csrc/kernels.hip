@@ -33,6 +33,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <type_traits>
 
 #include "pkv_launch.h"
 
@@ -1133,27 +1134,151 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 }
 
 // ---------------------------------------------------------------- chunked prefill
-// One wave per (kv head g, sequence s, group of NR query tiles).  A tile
-// holds tokens_per_tile = 16 / G query tokens of the chunk, row r = token
-// r / G, head r % G, so the G heads of a token share the K/V tile as in
-// decode; the NR tiles of a wave share every K/V fragment it loads (NR times
-// the MFMA work per byte).  Row r's query token sits at position p = L - C + j
-// of its sequence and sees tokens 0..p (causal); the wave walks tiles up to
-// its last row's position.  Rows past the chunk copy the group's last row and
-// are not written; rows with p < 0 (chunk longer than the context) are written
-// as zeros.
+// One workgroup per (kv head g, sequence s, item of 4 * NR query tiles).  A
+// query tile holds tokens_per_tile = 16 / G query tokens of the chunk, row
+// r = token r / G, head r % G, so the G heads of a token share every K/V
+// fragment as in decode; wave w owns NR consecutive query tiles.  Row r's
+// token sits at position p = L - C + j of its sequence and sees tokens 0..p
+// (causal); the workgroup walks the context up to its last row's position in
+// 32-token steps (two 16-token K/V tiles).  Each wave loads a quarter of every
+// step into registers PD steps ahead and publishes it to LDS (two buffers,
+// one barrier per step); all four waves run their query tiles against it, so
+// a K/V byte is fetched once per 4 * NR query tiles.  Rows past the chunk copy
+// the wave's last row and are not written; rows with p < 0 (chunk longer than
+// the context) are written as zeros.
+//
+// Per step a row tile costs 2 x (D / 32) score MFMAs and D / 16 P.V MFMAs of
+// 16x16x32 (the two tiles' 4-token fragments of a lane form one 8-element
+// operand, so P.V runs at the full bf16 rate), against about 40 VALU
+// instructions of online softmax.  Steps every row of the item sees in full
+// take a loop with no causal masking.
 template <int KIND, int D>
-struct PrefillRows {
-  static constexpr int NR = KIND == kF32 ? 1 : (D == 128 ? 2 : 4);  // row tiles per wave (register bound)
-  static constexpr int S = 2;                  // K/V register buffers
+struct PrefillCfg {
+  using T = Tile<KIND, D>;
+  static constexpr int NR = KIND == kF32 ? 1 : 2;  // query tiles per wave
+  static constexpr int PD = 2;                      // 32-token steps in flight per wave
+  // Each wave loads NL pieces of W bytes per lane of each 16-token K tile and
+  // as many of the V tile, so the four waves split a step evenly, unbranched.
+  static constexpr int W = T::BYTES / 256 < 16 ? T::BYTES / 256 : 16;
+  static constexpr int NL = T::BYTES / (256 * W);
+  static constexpr int FPC = W / T::VB;  // V fragments per loaded piece
+  static constexpr int PER_STEP = 2 * NL;  // pieces of K (and of V) per lane per step
+  static_assert(NL >= 1 && FPC >= 1, "tile split");
 };
 
-template <int KIND, int D, int S, int SH>
-__device__ __forceinline__ void prefill_group(const PrefillArgs& a, QLds<KIND, D>* qs, int s,
-                                              int g, int grp) {
+template <int KIND, int D>
+struct KVLds {  // one 16-token K/V tile in fragment order: [chunk][lane]
+  u32x4 k[Tile<KIND, D>::NK][64];
+  typename Tile<KIND, D>::V v[Tile<KIND, D>::NT][64];
+};
+
+// One 32-token step (tiles 2u and 2u + 1) in LDS.  K: per tile, fragment
+// order.  V: the two tiles' fragments of a lane side by side, v[nt][lane] =
+// {tile 2u, tile 2u + 1}, so one LDS read yields a P.V operand.
+template <int KIND, int D>
+struct PfStep {
   using T = Tile<KIND, D>;
-  constexpr int NR = PrefillRows<KIND, D>::NR;
-  constexpr int NW = 1;
+  u32x4 k[2][T::NK][64];
+  typename T::V v[T::NT][64][2];
+};
+
+template <int ES>
+struct ElemOf;
+template <>
+struct ElemOf<1> {
+  using T = uint8_t;
+};
+template <>
+struct ElemOf<2> {
+  using T = uint16_t;
+};
+template <>
+struct ElemOf<4> {
+  using T = uint32_t;
+};
+
+// Zero the elements of a V piece (consecutive tokens of one dim) from token
+// index `lim` of the piece on: V rows past the sequence may hold anything.
+template <int ES, typename PT>
+__device__ __forceinline__ PT zero_from(PT v, int lim) {
+  constexpr int N = sizeof(PT) / ES;
+  struct A {
+    typename ElemOf<ES>::T e[N];
+  };
+  A x = bitcast<A>(v);
+#pragma unroll
+  for (int e = 0; e < N; ++e)
+    if (e >= lim) x.e[e] = 0;
+  return bitcast<PT>(x);
+}
+
+// +inf in a scalar register the compiler cannot see through (a plain s_mov,
+// no memory access): med3(a, b, +inf) = max(a, b) then stays one v_med3
+// instead of being folded into a max that first quiets NaN operands.
+__device__ __forceinline__ float opaque_inf() {
+  float r;
+  asm("s_mov_b32 %0, 0x7f800000" : "=s"(r));
+  return r;
+}
+
+// Row max over the 16 lanes of a head (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float row_max(float v, float pinf) {
+  uint32_t u = __float_as_uint(v);
+  auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __builtin_amdgcn_fmed3f(__uint_as_float(s16[0]), __uint_as_float(s16[1]), pinf);
+  u = __float_as_uint(v);
+  auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_amdgcn_fmed3f(__uint_as_float(s32[0]), __uint_as_float(s32[1]), pinf);
+}
+
+// S^T[token 4*q4+i][row r] of one 16-token tile from its K fragments (LDS)
+// and the row tile's Q^T fragments (registers).
+template <int KIND, int D>
+__device__ __forceinline__ f32x4 pf_scores(const u32x4 (&kf)[Tile<KIND, D>::NK],
+                                           const u32x4 (&q)[Tile<KIND, D>::NQ]) {
+  using T = Tile<KIND, D>;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (KIND == kBF16) {
+#pragma unroll
+    for (int j = 0; j < T::NK; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(kf[j]), bitcast<bf16x8>(q[j]), acc, 0, 0, 0);
+  } else if constexpr (KIND == kFP8) {
+#pragma unroll
+    for (int j = 0; j < T::NK; ++j) {
+      u32x4 lo, hi;
+      fp8x16_to_bf16(kf[j], lo, hi);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(lo), bitcast<bf16x8>(q[2 * j]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(hi), bitcast<bf16x8>(q[2 * j + 1]), acc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < T::NK; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf[j][e]), __uint_as_float(q[j][e]), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Online-softmax state of one row tile: running max m (log2 units), the
+// bump threshold m + kLazyMax, the fp32 sum of the weights, and O^T.
+template <int KIND, int D>
+struct PfState {
+  float m, thr, l;
+  Acc<KIND, D> acc;
+};
+
+template <int KIND, int D, int SH>
+__device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, D>* kv, int w,
+                                             int s, int g, int item) {
+  using T = Tile<KIND, D>;
+  using C_ = PrefillCfg<KIND, D>;
+  using VT = typename T::V;
+  using PT = typename VecOf<C_::W>::T;
+  struct Parts {
+    VT p[C_::FPC];
+  };
+  constexpr int NR = C_::NR, PD = C_::PD, NL = C_::NL, W = C_::W, FPC = C_::FPC;
   constexpr int shift = SH;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, q4 = lane >> 4;
@@ -1162,43 +1287,63 @@ __device__ __forceinline__ void prefill_group(const PrefillArgs& a, QLds<KIND, D
   const int q0 = qst[s], C = qst[s + 1] - q0;
   int Ls = as_const(a.context_lens)[s];
   Ls = Ls < 0 ? 0 : (Ls > a.max_context_len ? a.max_context_len : Ls);
-  const int jbase = grp * NQ * NR;  // first chunk token of the group
-  const int jlast = (jbase + NQ * NR < C ? jbase + NQ * NR : C) - 1;
-  const int Lmax = Ls - C + jlast + 1;  // wave-uniform: tokens the group's last row sees
+  const int per_wave = NQ * NR;
+  const int ibase = item * 4 * per_wave;               // first chunk token of the item
+  const int ilast = (ibase + 4 * per_wave < C ? ibase + 4 * per_wave : C) - 1;
+  const int Lmax = Ls - C + ilast + 1;                  // tokens the item's last row sees
+  const int Lmin = Ls - C + ibase + 1;                  // ... and its first row
+  const int jbase = ibase + w * per_wave;               // this wave's first token
+  const int jlast = jbase + per_wave - 1 < ilast ? jbase + per_wave - 1 : ilast;
+  const int jfall = jlast >= jbase ? jlast : ilast;     // stand-in for rows past the chunk
   const int jl = r / G, hh = r % G;
+
+  const float pinf = opaque_inf();
+  const bool qneg = a.score_scale_log2 < 0.f;  // fold the sign into Q (exact)
+  const float scl = qneg ? -a.score_scale_log2 : a.score_scale_log2;
+  const uint32_t qflip = !qneg ? 0u : (KIND == kF32 ? 0x80000000u : 0x80008000u);
   int L[NR];
   bool row_ok[NR];
-#pragma unroll
-  for (int k = 0; k < NR; ++k) {
-    const int j = jbase + k * NQ + jl;
-    row_ok[k] = r < NQ * G && j < C;
-    const int Lrow = Ls - C + (row_ok[k] ? j : jlast) + 1;
-    L[k] = Lrow > 1 ? Lrow : 1;  // empty rows look at token 0, then write zeros
-  }
-
-  // Q^T fragments of the NR tiles, staged in this wave's LDS.  Lane l stages
-  // the fragment of lane l ^ 1, so every read below comes from another lane's
-  // write and stays an LDS read (the tiles do not fit in registers).
+  u32x4 q[NR][T::NQ];  // Q^T fragments, kept in registers for the whole item
   {
     constexpr int QES = KIND == kF32 ? 4 : 2;
-    const int pl = lane ^ 1, pr = pl & 15, pq4 = pl >> 4;
-    const int pjl = pr / G, phh = pr % G;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      const int j = jbase + k * NQ + pjl;
-      const int jj = pr < NQ * G && j < C ? j : jlast;
+      const int j = jbase + k * NQ + jl;
+      row_ok[k] = r < NQ * G && j <= jlast;
+      const int jj = row_ok[k] ? j : jfall;
+      const int Lrow = Ls - C + jj + 1;
+      L[k] = Lrow > 1 ? Lrow : 1;  // empty rows look at token 0, then write zeros
       const gchar_p qrow = (gchar_p) static_cast<const char*>(a.q) +
-                           ((int64_t)(q0 + jj) * Hq + g * G + phh) * D * QES;
+                           ((int64_t)(q0 + jj) * Hq + g * G + (r < NQ * G ? hh : 0)) * D * QES;
 #pragma unroll
       for (int jq = 0; jq < T::NQ; ++jq) {
         int off;
         if constexpr (KIND == kFP8)
-          off = ((jq >> 1) * 4 + pq4) * 32 + (jq & 1) * 16;
+          off = ((jq >> 1) * 4 + q4) * 32 + (jq & 1) * 16;
         else
-          off = (jq * 4 + pq4) * 16;
-        qs[k].qf[jq][pl] = *reinterpret_cast<gptr<u32x4>>(qrow + off);
+          off = (jq * 4 + q4) * 16;
+        q[k][jq] = *reinterpret_cast<gptr<u32x4>>(qrow + off) ^ qflip;
       }
     }
+  }
+
+  // This lane's pieces of a 16-token tile: byte t of the tile in pool order
+  // lies at row * (row bytes << shift) + (t mod row bytes) from the tile's
+  // start (K rows are 16 tokens x 16 bytes, V rows 16 tokens of one dim).  K
+  // pieces land in LDS at t (pool order is fragment order); a V piece holds
+  // FPC 4-token fragments of dim d, stored to [d / 16][q4 * 16 + d % 16].
+  uint32_t ksrc[NL], kdst[NL], vsrc[NL], vdst[NL];
+  int vtok[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const uint32_t t = (uint32_t)(((i * 4 + w) * 64 + lane) * W);
+    ksrc[i] = ((t >> 8) << (8 + shift)) + (t & 255u);
+    kdst[i] = t;
+    constexpr uint32_t VR = 16u * T::ES;  // V row bytes of a tile
+    const uint32_t d = t / VR, tk = (t % VR) / T::ES;
+    vsrc[i] = d * (VR << shift) + t % VR;
+    vdst[i] = ((d >> 4) * 64u + (tk >> 2) * 16u + (d & 15u)) * (2 * T::VB);
+    vtok[i] = (int)tk;
   }
 
   const cptr<int32_t> tbl = as_const(a.block_tables) + (int64_t)s * a.max_blocks;
@@ -1206,56 +1351,202 @@ __device__ __forceinline__ void prefill_group(const PrefillArgs& a, QLds<KIND, D
   const char* vbase = static_cast<const char*>(a.v_cache) + ((int64_t)g * T::BYTES << shift);
   const int64_t bstride = (int64_t)a.num_kv_heads * T::BYTES << shift;
   const int64_t last_block = a.num_blocks - 1;
-  const TileOffsets toff = tile_offsets<KIND, D>(lane, r, q4, shift);
-  auto tile_of = [&](int b, gchar_p& kt, gchar_p& vt) {
-    int64_t phys = __builtin_amdgcn_readfirstlane(tbl[b >> shift]);
-    phys = phys < 0 ? 0 : (phys > last_block ? last_block : phys);
-    const int half = b & ((1 << shift) - 1);
-    kt = uniform_ptr(kbase + phys * bstride + half * (kBS * 16));
-    vt = uniform_ptr(vbase + phys * bstride + half * (kBS * T::ES));
-  };
+  const int n16 = Lmax > 0 ? (Lmax + kBS - 1) / kBS : 0;  // 16-token tiles to read
+  const int n32 = (n16 + 1) >> 1;                           // steps
+  // steps every row of the item sees in full, rounded down to a whole
+  // number of slot pairs so the masked loop starts on slot 0
+  int u_full = Lmin > 0 ? Lmin / (2 * kBS) : 0;
+  u_full = (u_full < n32 ? u_full : n32) & ~1;
 
-  RunState<KIND, D> st[NR];
-#pragma unroll
-  for (int k = 0; k < NR; ++k) st[k].init();
-  const int b_end = Lmax > 0 ? (Lmax + kBS - 1) / kBS : 0;
-  int b = 0;
-  if (b < b_end) {
-    Frags<KIND, D> f0, f1, f2, f3;
-    gchar_p kt, vt;
-#define PKV_PREFETCH(BUF, AHEAD)                          \
-  tile_of(min(b + (AHEAD)*NW, b_end - 1), kt, vt);        \
-  load_tile<KIND, D, SH == 0>(BUF, kt, vt, toff);
-#define PKV_STAGE(CUR, NXT)                                                               \
-  PKV_PREFETCH(NXT, S - 1)                                                                \
-  _Pragma("unroll") for (int k = 0; k < NR; ++k) {                                        \
-    process_block<KIND, D>(st[k], CUR, qs[k], b, L[k], Lmax, a.score_scale_log2, lane, q4); \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-  }                                                                                       \
-  b += NW;                                                                                \
-  if (b >= b_end) break;
-    PKV_PREFETCH(f0, 0)
-    if constexpr (S >= 3) { PKV_PREFETCH(f1, 1) }
-    if constexpr (S >= 4) { PKV_PREFETCH(f2, 2) }
-    if constexpr (S == 2) {
-      for (;;) { PKV_STAGE(f0, f1) PKV_STAGE(f1, f0) }
-    } else if constexpr (S == 3) {
-      for (;;) { PKV_STAGE(f0, f2) PKV_STAGE(f1, f0) PKV_STAGE(f2, f1) }
-    } else {
-      for (;;) { PKV_STAGE(f0, f3) PKV_STAGE(f1, f0) PKV_STAGE(f2, f1) PKV_STAGE(f3, f2) }
-    }
-#undef PKV_STAGE
-#undef PKV_PREFETCH
-  }
+  PfState<KIND, D> st[NR];
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
-    const float l_run = sum_across_groups(st[k].l);
-    const float e_run = sum_across_groups(st[k].e);
+    st[k].m = -INFINITY;
+    st[k].thr = -INFINITY;
+    st[k].l = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < T::NT; ++nt) st[k].acc.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  PT sk[PD][2][NL], sv[PD][2][NL];
+  auto load_slot = [&](PT (&dk)[2][NL], PT (&dv)[2][NL], int u) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int t16 = 2 * u + h;
+      t16 = t16 < n16 - 1 ? t16 : n16 - 1;
+      int64_t phys = __builtin_amdgcn_readfirstlane(tbl[t16 >> shift]);
+      phys = phys < 0 ? 0 : (phys > last_block ? last_block : phys);
+      const int half = t16 & ((1 << shift) - 1);
+      const gchar_p kt = uniform_ptr(kbase + phys * bstride + half * (kBS * 16));
+      const gchar_p vt = uniform_ptr(vbase + phys * bstride + half * (kBS * T::ES));
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        gptr<PT> pk = reinterpret_cast<gptr<PT>>(kt + ksrc[i]);
+        gptr<PT> pv = reinterpret_cast<gptr<PT>>(vt + vsrc[i]);
+        dk[h][i] = SH == 0 ? __builtin_nontemporal_load(pk) : *pk;
+        dv[h][i] = SH == 0 ? __builtin_nontemporal_load(pv) : *pv;
+      }
+    }
+  };
+  // Publish a step to LDS.  On the step holding the sequence end (only in
+  // the masked loop) V elements past Lmax are zeroed: their weights are 0
+  // but the slots may hold NaN.
+  auto store_slot = [&](const PT (&dk)[2][NL], const PT (&dv)[2][NL], PfStep<KIND, D>& dst,
+                        int u, bool tail) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      char* kb = reinterpret_cast<char*>(dst.k[h]);
+      char* vb = reinterpret_cast<char*>(dst.v) + h * T::VB;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        *reinterpret_cast<PT*>(kb + kdst[i]) = dk[h][i];
+        PT v = dv[h][i];
+        if (tail) v = zero_from<T::ES>(v, Lmax - (u * 2 + h) * kBS - vtok[i]);
+        const Parts pp = bitcast<Parts>(v);
+#pragma unroll
+        for (int f = 0; f < FPC; ++f)
+          *reinterpret_cast<VT*>(vb + vdst[i] + f * 16 * (2 * T::VB)) = pp.p[f];
+      }
+    }
+  };
+  // Scores, online softmax and P.V of step u for every row tile.
+  auto compute = [&](const PfStep<KIND, D>& t, int u, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    f32x4 sc[NR][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 kf[T::NK];
+#pragma unroll
+      for (int j = 0; j < T::NK; ++j) kf[j] = t.k[h][j][lane];
+#pragma unroll
+      for (int k = 0; k < NR; ++k) sc[k][h] = pf_scores<KIND, D>(kf, q[k]);
+    }
+    using PB = typename std::conditional<KIND == kF32, f32x4, bf16x8>::type;
+    PB pw[NR][KIND == kF32 ? 2 : 1];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      // Raw scores; the scale (> 0: a negative one was moved into Q) is
+      // applied inside the exponent, p = 2^(s * scale - m).
+      float x[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = sc[k][h][i];
+          if (MASK) v = u * 2 * kBS + h * kBS + 4 * q4 + i < L[k] ? v : -INFINITY;
+          x[h * 4 + i] = v;
+        }
+      const float m01 = __builtin_amdgcn_fmed3f(x[0], x[1], pinf);
+      const float m23 = __builtin_amdgcn_fmed3f(x[2], x[3], pinf);
+      const float m45 = __builtin_amdgcn_fmed3f(x[4], x[5], pinf);
+      const float m67 = __builtin_amdgcn_fmed3f(x[6], x[7], pinf);
+      const float mraw = row_max(fmaxf(fmaxf(m01, m23), fmaxf(m45, m67)), pinf);
+      const float mx = mraw * scl;       // NaN only if the whole step is masked and scl = 0
+      const bool bump = mx > st[k].thr;  // always true on a row's first step
+      if (__builtin_amdgcn_ballot_w64(bump)) {
+        const float m_new = bump ? mx : st[k].m;
+        const float alpha = __builtin_amdgcn_exp2f(st[k].m - m_new);
+        st[k].m = m_new;
+        st[k].thr = m_new + kLazyMax;
+        st[k].l *= alpha;
+#pragma unroll
+        for (int nt = 0; nt < T::NT; ++nt) st[k].acc.o[nt] *= alpha;
+      }
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], scl, -st[k].m));
+        if (MASK) p[i] = x[i] == -INFINITY ? 0.f : p[i];
+      }
+      st[k].l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      if constexpr (KIND == kF32) {
+        pw[k][0] = f32x4{p[0], p[1], p[2], p[3]};
+        pw[k][1] = f32x4{p[4], p[5], p[6], p[7]};
+      } else {
+        const bf16x2 p01 = __builtin_convertvector(f32x2{p[0], p[1]}, bf16x2);
+        const bf16x2 p23 = __builtin_convertvector(f32x2{p[2], p[3]}, bf16x2);
+        const bf16x2 p45 = __builtin_convertvector(f32x2{p[4], p[5]}, bf16x2);
+        const bf16x2 p67 = __builtin_convertvector(f32x2{p[6], p[7]}, bf16x2);
+        const u32x4 pp = {bitcast<uint32_t>(p01), bitcast<uint32_t>(p23), bitcast<uint32_t>(p45),
+                          bitcast<uint32_t>(p67)};
+        pw[k][0] = bitcast<bf16x8>(pp);
+      }
+    }
+    // O^T[d][row] += V^T . P^T over the step's 32 tokens
+#pragma unroll
+    for (int nt = 0; nt < T::NT; ++nt) {
+      const VT va = t.v[nt][lane][0], vb = t.v[nt][lane][1];
+      if constexpr (KIND == kF32) {
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+          f32x4 o = st[k].acc.o[nt];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(va[i]), pw[k][0][i], o, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb[i]), pw[k][1][i], o, 0, 0, 0);
+          st[k].acc.o[nt] = o;
+        }
+      } else {
+        u32x2 lo, hi;
+        if constexpr (KIND == kBF16) {
+          lo = va;
+          hi = vb;
+        } else {
+          lo = bitcast<u32x2>(fp8x4_to_bf16x4(va));
+          hi = bitcast<u32x2>(fp8x4_to_bf16x4(vb));
+        }
+        const bf16x8 vv = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+          st[k].acc.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pw[k][0], st[k].acc.o[nt], 0, 0, 0);
+      }
+    }
+  };
+
+  if (n32 > 0) {
+#pragma unroll
+    for (int i = 0; i < PD; ++i) load_slot(sk[i], sv[i], i);
+    int u = 0;
+    // Stage I: publish slot I (step u) to LDS buffer I, refill the slot with
+    // step u + PD, then run the row tiles against step u.  The buffer written
+    // here was last read two stages ago, before the previous stage's
+    // barrier, so one barrier per step suffices.
+#define PKV_PF_STAGE(I, MASK)                                                     \
+  {                                                                               \
+    store_slot(sk[I], sv[I], kv[I], u, MASK && (u + 1) * 2 * kBS > Lmax);         \
+    __syncthreads();                                                              \
+    load_slot(sk[I], sv[I], u + PD);                                              \
+    compute(kv[I], u, std::integral_constant<bool, MASK>());                      \
+    ++u;                                                                          \
+  }
+    static_assert(PD == 2, "the stage loops below are written for 2 slots");
+    while (u < u_full) {
+      PKV_PF_STAGE(0, false)
+      PKV_PF_STAGE(1, false)
+    }
+    for (;;) {
+      PKV_PF_STAGE(0, true)
+      if (u >= n32) break;
+      PKV_PF_STAGE(1, true)
+      if (u >= n32) break;
+    }
+#undef PKV_PF_STAGE
+  }
+
+#pragma unroll
+  for (int k = 0; k < NR; ++k) {
+    uint32_t lu = __float_as_uint(st[k].l);
+    auto s16 = __builtin_amdgcn_permlane16_swap(lu, lu, false, false);
+    float lsum = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    lu = __float_as_uint(lsum);
+    auto s32 = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
+    lsum = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
     if (!row_ok[k]) continue;
     const int j = jbase + k * NQ + jl;
     const bool empty = Ls - C + j + 1 <= 0;
     const int64_t row = (int64_t)(q0 + j) * Hq + g * G + hh;
-    const float inv = !empty && l_run > 0.f ? a.v_scale / l_run : 0.f;
+    const float inv = !empty && lsum > 0.f ? a.v_scale / lsum : 0.f;
 #pragma unroll
     for (int nt = 0; nt < T::NT; ++nt) {
       const int d = nt * 16 + 4 * q4;
@@ -1269,34 +1560,34 @@ __device__ __forceinline__ void prefill_group(const PrefillArgs& a, QLds<KIND, D
       }
     }
     if (q4 == 0 && a.lse)
-      a.lse[row] = !empty && e_run > 0.f ? (st[k].m + __builtin_amdgcn_logf(e_run)) * kLn2 : -INFINITY;
+      a.lse[row] = !empty && lsum > 0.f ? (st[k].m + __builtin_amdgcn_logf(lsum)) * kLn2 : -INFINITY;
   }
 }
 
-// Items (g, s, group) lie head major: item g * TQ + ct[s] + group, ct =
-// prefix sums of the sequences' group counts, built in LDS by every
-// workgroup.  Workgroup b takes items ((b mod 8) * (nWG / 8) + b / 8) * NW + w,
-// so one XCD works through consecutive groups of the same sequences and
-// shares their K/V tiles in its L2.
-template <int KIND, int D, int NW, int S, int SH>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+// Items (g, s, item) lie head major: item g * TQ + ct[s] + i, ct = prefix
+// sums of the sequences' item counts, built in LDS by every workgroup.
+// Workgroup b takes item (b mod 8) * (nWG / 8) + b / 8, so one XCD works
+// through consecutive items of the same sequences and shares their K/V tiles
+// in its L2.
+template <int KIND, int D, int SH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
-  constexpr int NR = PrefillRows<KIND, D>::NR;
-  __shared__ QLds<KIND, D> qs[NW][NR];
+  constexpr int NR = PrefillCfg<KIND, D>::NR;
+  __shared__ PfStep<KIND, D> kv[2];
   __shared__ int lct[kPrefillMaxSeqs + 1];
-  __shared__ int wsums[NW];
+  __shared__ int wsums[4];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nseq = a.num_seqs, H = a.num_kv_heads;
-  const int per = a.tokens_per_tile * NR;  // query tokens per item
+  const int per = a.tokens_per_tile * NR * 4;  // query tokens per item
   {
     const int tid = threadIdx.x;
     int carry = 0;
-    for (int c0 = 0; c0 < nseq; c0 += NW * 64) {
+    for (int c0 = 0; c0 < nseq; c0 += 256) {
       const int s = c0 + tid;
       int C = s < nseq ? a.query_start[s + 1] - a.query_start[s] : 0;
       C = C < 0 ? 0 : C;
       int tot;
-      const int e = block_exclusive_scan<NW>((C + per - 1) / per, wsums, &tot);
+      const int e = block_exclusive_scan<4>((C + per - 1) / per, wsums, &tot);
       if (s < nseq) lct[s] = carry + e;
       carry += tot;
     }
@@ -1305,15 +1596,15 @@ void prefill_kernel(PrefillArgs a) {
   }
   const int TQ = lct[nseq];
   const int groups = gridDim.x;
-  const int64_t k = ((int64_t)(blockIdx.x & 7) * (groups >> 3) + (blockIdx.x >> 3)) * NW + w;
-  if (k >= (int64_t)H * TQ) return;
+  const int64_t k = (int64_t)(blockIdx.x & 7) * (groups >> 3) + (blockIdx.x >> 3);
+  if (k >= (int64_t)H * TQ) return;  // the whole workgroup
   const int g = (int)(k / TQ), rem = (int)(k % TQ);
   int lo = 0, hi = nseq;  // largest s with lct[s] <= rem
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (lct[mid] <= rem) lo = mid; else hi = mid;
   }
-  prefill_group<KIND, D, S, SH>(a, qs[w], lo, g, rem - lct[lo]);
+  prefill_item<KIND, D, SH>(a, kv, w, lo, g, rem - lct[lo]);
 }
 
 // Register buffers (prefetch depth + 1) per cache dtype, at two waves per
@@ -1466,22 +1757,22 @@ hipError_t launch_prefill(const PrefillArgs& a, int cache, int D, int64_t num_ro
                           hipStream_t stream, bool* supported) {
   *supported = true;
   if (a.num_seqs == 0 || num_rows == 0) return hipSuccess;
-  // waves: at most one per group of NR query tiles; groups <= rows / tokens
-  // per group + one partial group per sequence
-  const int per = a.tokens_per_tile * (cache == kF32 ? 1 : (D == 128 ? 2 : 4));
-  const int64_t tiles = (num_rows + per - 1) / per + a.num_seqs;
-  int64_t groups = ((int64_t)a.num_kv_heads * tiles + kWavesPerGroup - 1) / kWavesPerGroup;
+  // one workgroup per item of 4 * NR query tiles; items <= rows / tokens per
+  // item + one partial item per sequence
+  const int nr = cache == kF32 ? PrefillCfg<kF32, 128>::NR : PrefillCfg<kBF16, 128>::NR;
+  const int per = a.tokens_per_tile * nr * 4;
+  const int64_t items = (num_rows + per - 1) / per + a.num_seqs;
+  int64_t groups = (int64_t)a.num_kv_heads * items;
   groups = (groups + 7) / 8 * 8;
   if (groups > INT32_MAX) {
     *supported = false;
     return hipSuccess;
   }
-  const dim3 grid((unsigned)groups), block(kWavesPerGroup * 64);
-#define PKV_PF(C_, D_, SH_)                                                                   \
-  if (cache == C_ && D == D_ && a.block_shift == SH_) {                                       \
-    hipLaunchKernelGGL((prefill_kernel<C_, D_, kWavesPerGroup, PrefillRows<C_, D_>::S, SH_>), grid, \
-                       block, 0, stream, a);                                                  \
-    return hipGetLastError();                                                                 \
+  const dim3 grid((unsigned)groups), block(256);
+#define PKV_PF(C_, D_, SH_)                                                           \
+  if (cache == C_ && D == D_ && a.block_shift == SH_) {                               \
+    hipLaunchKernelGGL((prefill_kernel<C_, D_, SH_>), grid, block, 0, stream, a);     \
+    return hipGetLastError();                                                         \
   }
   PKV_PF(kF32, 64, 0) PKV_PF(kF32, 128, 0) PKV_PF(kBF16, 64, 0) PKV_PF(kBF16, 128, 0)
   PKV_PF(kFP8, 64, 0) PKV_PF(kFP8, 128, 0) PKV_PF(kF32, 64, 1) PKV_PF(kF32, 128, 1)

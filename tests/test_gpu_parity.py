@@ -475,7 +475,7 @@ def _paged_batch(gen, cache, D, Hkv, lens, bs=16, seed=0):
                 vsc=vsc, bs=bs)
 
 
-def _prefill_case(cache, D, grp, lens, chunks, bs=16, Hkv=2, label=""):
+def _prefill_case(cache, D, grp, lens, chunks, bs=16, Hkv=2, label="", scale=None):
     gen = torch.Generator().manual_seed(1000 + 97 * cache + D + 7 * grp + bs)
     b = _paged_batch(gen, cache, D, Hkv, lens, bs, seed=grp + D)
     Hq = Hkv * grp
@@ -485,7 +485,7 @@ def _prefill_case(cache, D, grp, lens, chunks, bs=16, Hkv=2, label=""):
     dq = _to_device(q, b["qd"])
     out_t = torch.float32 if cache == F32 else torch.bfloat16
     d_tables = torch.from_numpy(b["tables"]).cuda()
-    scale = 1 / math.sqrt(D)
+    scale = 1 / math.sqrt(D) if scale is None else scale
     p = pkv.make_prefill_params(dq, b["dk"], d_tables, len(lens), b["mb"] * bs, scale, b["ksc"],
                                 b["vsc"], out_t)
     out = torch.full((R, Hq, D), float("nan"), dtype=out_t, device="cuda")
@@ -527,6 +527,14 @@ def test_prefill_mixed_chunks(cache, D, group):
 @pytest.mark.parametrize("cache", [BF16, E4M3])
 def test_prefill_block_size_32(cache):
     _prefill_case(cache, 128, 4, PF_LENS, PF_CHUNKS, bs=32, label="bs32")
+
+
+@pytest.mark.parametrize("cache", [F32, BF16])
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_prefill_negative_and_zero_scale(cache, scale):
+    """The softmax scale is any finite number: a negative one flips which
+    keys dominate, zero gives uniform weights over the causal window."""
+    _prefill_case(cache, 64, 4, [40, 300, 77], [40, 33, 9], label=f"scale {scale}", scale=scale)
 
 
 def test_prefill_full_sequences_and_overlong_chunks():
