@@ -1356,7 +1356,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   // steps every row of the item sees in full, rounded down to a whole
   // number of slot pairs so the masked loop starts on slot 0
   int u_full = Lmin > 0 ? Lmin / (2 * kBS) : 0;
-  u_full = (u_full < n32 ? u_full : n32) & ~1;
+  u_full = u_full < n32 ? u_full : n32;
+  u_full -= u_full % PD;
 
   PfState<KIND, D> st[NR];
 #pragma unroll
@@ -1378,12 +1379,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       const int half = t16 & ((1 << shift) - 1);
       const gchar_p kt = uniform_ptr(kbase + phys * bstride + half * (kBS * 16));
       const gchar_p vt = uniform_ptr(vbase + phys * bstride + half * (kBS * T::ES));
+      // Default cache policy: every item of the sequence reads these tiles,
+      // and the items of a (head, sequence) pair run side by side on one XCD.
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        gptr<PT> pk = reinterpret_cast<gptr<PT>>(kt + ksrc[i]);
-        gptr<PT> pv = reinterpret_cast<gptr<PT>>(vt + vsrc[i]);
-        dk[h][i] = SH == 0 ? __builtin_nontemporal_load(pk) : *pk;
-        dv[h][i] = SH == 0 ? __builtin_nontemporal_load(pv) : *pv;
+        dk[h][i] = *reinterpret_cast<gptr<PT>>(kt + ksrc[i]);
+        dv[h][i] = *reinterpret_cast<gptr<PT>>(vt + vsrc[i]);
       }
     }
   };
@@ -1420,30 +1421,48 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
 #pragma unroll
       for (int k = 0; k < NR; ++k) sc[k][h] = pf_scores<KIND, D>(kf, q[k]);
     }
-    using PB = typename std::conditional<KIND == kF32, f32x4, bf16x8>::type;
-    PB pw[NR][KIND == kF32 ? 2 : 1];
+    // Raw scores; the scale (> 0: a negative one was moved into Q) is
+    // applied inside the exponent, p = 2^(s * scale - m).
+    float x[NR][8], mx[NR];
+    bool bump[NR];
+    bool any = false;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      // Raw scores; the scale (> 0: a negative one was moved into Q) is
-      // applied inside the exponent, p = 2^(s * scale - m).
-      float x[8];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = sc[k][h][i];
           if (MASK) v = u * 2 * kBS + h * kBS + 4 * q4 + i < L[k] ? v : -INFINITY;
-          x[h * 4 + i] = v;
+          x[k][h * 4 + i] = v;
         }
-      const float m01 = __builtin_amdgcn_fmed3f(x[0], x[1], pinf);
-      const float m23 = __builtin_amdgcn_fmed3f(x[2], x[3], pinf);
-      const float m45 = __builtin_amdgcn_fmed3f(x[4], x[5], pinf);
-      const float m67 = __builtin_amdgcn_fmed3f(x[6], x[7], pinf);
-      const float mraw = row_max(fmaxf(fmaxf(m01, m23), fmaxf(m45, m67)), pinf);
-      const float mx = mraw * scl;       // NaN only if the whole step is masked and scl = 0
-      const bool bump = mx > st[k].thr;  // always true on a row's first step
-      if (__builtin_amdgcn_ballot_w64(bump)) {
-        const float m_new = bump ? mx : st[k].m;
+      const float m01 = __builtin_amdgcn_fmed3f(x[k][0], x[k][1], pinf);
+      const float m23 = __builtin_amdgcn_fmed3f(x[k][2], x[k][3], pinf);
+      const float m45 = __builtin_amdgcn_fmed3f(x[k][4], x[k][5], pinf);
+      const float m67 = __builtin_amdgcn_fmed3f(x[k][6], x[k][7], pinf);
+      mx[k] = row_max(fmaxf(fmaxf(m01, m23), fmaxf(m45, m67)), pinf) * scl;
+      bump[k] = mx[k] > st[k].thr;  // always true on a row's first step; false for NaN
+      any = any || bump[k];
+    }
+    if constexpr (KIND != kF32 && NR == 2) {
+      // Issue order for the block above: the K fragment reads, the first
+      // row tile's score MFMAs, then its row max interleaved with the second
+      // tile's score MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::NK, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::NQ, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * T::NQ; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
+      }
+    }
+    // One branch for all row tiles (rarely taken past the first steps), so
+    // the exponentials and the P.V products below form one block the
+    // scheduler can interleave.  Lanes without a bump rescale by 2^0 = 1.
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int k = 0; k < NR; ++k) {
+        const float m_new = bump[k] ? mx[k] : st[k].m;
         const float alpha = __builtin_amdgcn_exp2f(st[k].m - m_new);
         st[k].m = m_new;
         st[k].thr = m_new + kLazyMax;
@@ -1451,11 +1470,16 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
 #pragma unroll
         for (int nt = 0; nt < T::NT; ++nt) st[k].acc.o[nt] *= alpha;
       }
+    }
+    using PB = typename std::conditional<KIND == kF32, f32x4, bf16x8>::type;
+    PB pw[NR][KIND == kF32 ? 2 : 1];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
       float p[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], scl, -st[k].m));
-        if (MASK) p[i] = x[i] == -INFINITY ? 0.f : p[i];
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[k][i], scl, -st[k].m));
+        if (MASK) p[i] = x[k][i] == -INFINITY ? 0.f : p[i];
       }
       st[k].l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       if constexpr (KIND == kF32) {
@@ -1502,6 +1526,18 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
           st[k].acc.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pw[k][0], st[k].acc.o[nt], 0, 0, 0);
       }
     }
+    if constexpr (KIND != kF32 && NR == 2) {
+      // Issue order: V fragment reads and the first tile's weights, then its
+      // P.V MFMAs interleaved with the second tile's weights, then the rest.
+      __builtin_amdgcn_sched_group_barrier(0x100, T::NT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 28, 0);
+#pragma unroll
+      for (int i = 0; i < T::NT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, T::NT, 0);
+    }
   };
 
   if (n32 > 0) {
@@ -1510,7 +1546,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
     int u = 0;
     // Stage I: publish slot I (step u) to LDS buffer I, refill the slot with
     // step u + PD, then run the row tiles against step u.  The buffer written
-    // here was last read two stages ago, before the previous stage's
+    // here was last read PD >= 2 stages ago, before the previous stage's
     // barrier, so one barrier per step suffices.
 #define PKV_PF_STAGE(I, MASK)                                                     \
   {                                                                               \
@@ -1520,16 +1556,26 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
     compute(kv[I], u, std::integral_constant<bool, MASK>());                      \
     ++u;                                                                          \
   }
-    static_assert(PD == 2, "the stage loops below are written for 2 slots");
+    static_assert(PD >= 2 && PD <= 4, "the stage loops below are written for 2 to 4 slots");
     while (u < u_full) {
       PKV_PF_STAGE(0, false)
       PKV_PF_STAGE(1, false)
+      if constexpr (PD >= 3) { PKV_PF_STAGE(2, false) }
+      if constexpr (PD >= 4) { PKV_PF_STAGE(3, false) }
     }
     for (;;) {
       PKV_PF_STAGE(0, true)
       if (u >= n32) break;
       PKV_PF_STAGE(1, true)
       if (u >= n32) break;
+      if constexpr (PD >= 3) {
+        PKV_PF_STAGE(2, true)
+        if (u >= n32) break;
+      }
+      if constexpr (PD >= 4) {
+        PKV_PF_STAGE(3, true)
+        if (u >= n32) break;
+      }
     }
 #undef PKV_PF_STAGE
   }
@@ -1573,7 +1619,7 @@ template <int KIND, int D, int SH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int NR = PrefillCfg<KIND, D>::NR;
-  __shared__ PfStep<KIND, D> kv[2];
+  __shared__ PfStep<KIND, D> kv[PrefillCfg<KIND, D>::PD];
   __shared__ int lct[kPrefillMaxSeqs + 1];
   __shared__ int wsums[4];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
