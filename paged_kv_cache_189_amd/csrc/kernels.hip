@@ -1353,11 +1353,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   const int64_t last_block = a.num_blocks - 1;
   const int n16 = Lmax > 0 ? (Lmax + kBS - 1) / kBS : 0;  // 16-token tiles to read
   const int n32 = (n16 + 1) >> 1;                           // steps
-  // steps every row of the item sees in full, rounded down to a whole
-  // number of slot pairs so the masked loop starts on slot 0
+  // Steps every row of the item sees in full (no causal masking needed).
   int u_full = Lmin > 0 ? Lmin / (2 * kBS) : 0;
   u_full = u_full < n32 ? u_full : n32;
-  u_full -= u_full % PD;
 
   PfState<KIND, D> st[NR];
 #pragma unroll
@@ -1388,9 +1386,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       }
     }
   };
-  // Publish a step to LDS.  On the step holding the sequence end (only in
-  // the masked loop) V elements past Lmax are zeroed: their weights are 0
-  // but the slots may hold NaN.
+  // Publish a step to LDS.  On the step holding the sequence end V elements
+  // past Lmax are zeroed: their weights are 0 but the slots may hold NaN.
   auto store_slot = [&](const PT (&dk)[2][NL], const PT (&dv)[2][NL], PfStep<KIND, D>& dst,
                         int u, bool tail) {
 #pragma unroll
@@ -1409,10 +1406,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       }
     }
   };
-  // Scores, online softmax and P.V of step u for every row tile.
-  auto compute = [&](const PfStep<KIND, D>& t, int u, auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    f32x4 sc[NR][2];
+
+  using PB = typename std::conditional<KIND == kF32, f32x4, bf16x8>::type;
+  constexpr int NPB = KIND == kF32 ? 2 : 1;
+  // S^T of a step for every row tile, from the step's K in LDS.
+  auto scores_of = [&](const PfStep<KIND, D>& t, f32x4 (&sc)[NR][2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       u32x4 kf[T::NK];
@@ -1421,10 +1419,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
 #pragma unroll
       for (int k = 0; k < NR; ++k) sc[k][h] = pf_scores<KIND, D>(kf, q[k]);
     }
-    // Raw scores; the scale (> 0: a negative one was moved into Q) is
-    // applied inside the exponent, p = 2^(s * scale - m).
-    float x[NR][8], mx[NR];
-    bool bump[NR];
+  };
+  // Raw scores of step u (past each row's causal bound -> -inf when MASK),
+  // their row max in log2 units, and whether it moves the running max.  The
+  // scale (> 0: a negative one was moved into Q) is applied inside the
+  // exponent, p = 2^(s * scale - m).
+  auto max_of = [&](const f32x4 (&sc)[NR][2], int u, auto masked, float (&x)[NR][8],
+                    float (&mx)[NR], bool (&bump)[NR], bool live) {
+    constexpr bool MASK = decltype(masked)::value;
     bool any = false;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
@@ -1441,38 +1443,28 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       const float m45 = __builtin_amdgcn_fmed3f(x[k][4], x[k][5], pinf);
       const float m67 = __builtin_amdgcn_fmed3f(x[k][6], x[k][7], pinf);
       mx[k] = row_max(fmaxf(fmaxf(m01, m23), fmaxf(m45, m67)), pinf) * scl;
-      bump[k] = mx[k] > st[k].thr;  // always true on a row's first step; false for NaN
+      bump[k] = live && mx[k] > st[k].thr;  // always true on a row's first step; false for NaN
       any = any || bump[k];
     }
-    if constexpr (KIND != kF32 && NR == 2) {
-      // Issue order for the block above: the K fragment reads, the first
-      // row tile's score MFMAs, then its row max interleaved with the second
-      // tile's score MFMAs.
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::NK, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::NQ, 0);
+    return any;
+  };
+  // Move the running max before a step's weights are formed; O must already
+  // hold every earlier step.  Lanes without a bump rescale by 2^0 = 1.
+  auto rescale = [&](const float (&mx)[NR], const bool (&bump)[NR]) {
 #pragma unroll
-      for (int i = 0; i < 2 * T::NQ; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
-      }
+    for (int k = 0; k < NR; ++k) {
+      const float m_new = bump[k] ? mx[k] : st[k].m;
+      const float alpha = __builtin_amdgcn_exp2f(st[k].m - m_new);
+      st[k].m = m_new;
+      st[k].thr = m_new + kLazyMax;
+      st[k].l *= alpha;
+#pragma unroll
+      for (int nt = 0; nt < T::NT; ++nt) st[k].acc.o[nt] *= alpha;
     }
-    // One branch for all row tiles (rarely taken past the first steps), so
-    // the exponentials and the P.V products below form one block the
-    // scheduler can interleave.  Lanes without a bump rescale by 2^0 = 1.
-    if (__builtin_amdgcn_ballot_w64(any)) {
-#pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        const float m_new = bump[k] ? mx[k] : st[k].m;
-        const float alpha = __builtin_amdgcn_exp2f(st[k].m - m_new);
-        st[k].m = m_new;
-        st[k].thr = m_new + kLazyMax;
-        st[k].l *= alpha;
-#pragma unroll
-        for (int nt = 0; nt < T::NT; ++nt) st[k].acc.o[nt] *= alpha;
-      }
-    }
-    using PB = typename std::conditional<KIND == kF32, f32x4, bf16x8>::type;
-    PB pw[NR][KIND == kF32 ? 2 : 1];
+  };
+  // Weights of a step, summed into l (fp32) and packed as P.V operands.
+  auto weights_of = [&](const float (&x)[NR][8], auto masked, PB (&pw)[NR][NPB]) {
+    constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       float p[8];
@@ -1495,7 +1487,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
         pw[k][0] = bitcast<bf16x8>(pp);
       }
     }
-    // O^T[d][row] += V^T . P^T over the step's 32 tokens
+  };
+  // O^T[d][row] += V^T . P^T over a step's 32 tokens.
+  auto pv_of = [&](const PfStep<KIND, D>& t, const PB (&pw)[NR][NPB]) {
 #pragma unroll
     for (int nt = 0; nt < T::NT; ++nt) {
       const VT va = t.v[nt][lane][0], vb = t.v[nt][lane][1];
@@ -1526,54 +1520,77 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
           st[k].acc.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pw[k][0], st[k].acc.o[nt], 0, 0, 0);
       }
     }
-    if constexpr (KIND != kF32 && NR == 2) {
-      // Issue order: V fragment reads and the first tile's weights, then its
-      // P.V MFMAs interleaved with the second tile's weights, then the rest.
-      __builtin_amdgcn_sched_group_barrier(0x100, T::NT, 0);
-      __builtin_amdgcn_sched_group_barrier(0x402, 28, 0);
-#pragma unroll
-      for (int i = 0; i < T::NT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, T::NT, 0);
-    }
   };
 
   if (n32 > 0) {
+    // Software pipeline over steps.  Stage u publishes step u + 1 and runs
+    // the MFMAs of step u + 1's scores and step u's P.V while the VALU forms
+    // step u's weights and step u + 1's row max, so matrix and vector work
+    // of one wave overlap.  Step j lives in LDS buffer j mod 3: stage u reads
+    // buffers u and u + 1 and writes u + 1, last read at stage u - 2 (before
+    // the previous stage's barrier), so one barrier per stage suffices.
+    // Register slot j mod PD holds step j from its load, issued PD stages
+    // ahead, until it is published.
+    float x[NR][8];
 #pragma unroll
     for (int i = 0; i < PD; ++i) load_slot(sk[i], sv[i], i);
+    store_slot(sk[0], sv[0], kv[0], 0, 2 * kBS > Lmax);
+    __syncthreads();
+    load_slot(sk[0], sv[0], PD);
+    {
+      f32x4 sc[NR][2];
+      scores_of(kv[0], sc);
+      float mx[NR];
+      bool bump[NR];
+      if (__builtin_amdgcn_ballot_w64(max_of(sc, 0, std::true_type(), x, mx, bump, true)))
+        rescale(mx, bump);
+    }
     int u = 0;
-    // Stage I: publish slot I (step u) to LDS buffer I, refill the slot with
-    // step u + PD, then run the row tiles against step u.  The buffer written
-    // here was last read PD >= 2 stages ago, before the previous stage's
-    // barrier, so one barrier per step suffices.
-#define PKV_PF_STAGE(I, MASK)                                                     \
-  {                                                                               \
-    store_slot(sk[I], sv[I], kv[I], u, MASK && (u + 1) * 2 * kBS > Lmax);         \
-    __syncthreads();                                                              \
-    load_slot(sk[I], sv[I], u + PD);                                              \
-    compute(kv[I], u, std::integral_constant<bool, MASK>());                      \
-    ++u;                                                                          \
+#define PKV_PF_STAGE(J, MASK)                                                            \
+  {                                                                                      \
+    constexpr int BC = (J) % 3, BN = ((J) + 1) % 3, SL = ((J) + 1) % PD;                 \
+    const bool live = u + 1 < n32;                                                       \
+    store_slot(sk[SL], sv[SL], kv[BN], u + 1, MASK && (u + 2) * 2 * kBS > Lmax);         \
+    __syncthreads();                                                                     \
+    load_slot(sk[SL], sv[SL], u + 1 + PD);                                               \
+    f32x4 scn[NR][2];                                                                    \
+    scores_of(kv[BN], scn);                                                              \
+    PB pw[NR][NPB];                                                                      \
+    weights_of(x, std::integral_constant<bool, MASK>(), pw);                             \
+    pv_of(kv[BC], pw);                                                                   \
+    float mx[NR];                                                                        \
+    bool bump[NR];                                                                       \
+    const bool any = max_of(scn, u + 1, std::integral_constant<bool, MASK>(), x, mx, bump, live); \
+    if (__builtin_amdgcn_ballot_w64(any)) rescale(mx, bump);                             \
+    ++u;                                                                                 \
   }
-    static_assert(PD >= 2 && PD <= 4, "the stage loops below are written for 2 to 4 slots");
-    while (u < u_full) {
+    // Stage u may skip masking when steps u and u + 1 are seen in full.
+    constexpr int U = PD % 3 == 0 ? PD : 3 * PD;  // stages per unrolled round
+    const int u_plain = u_full >= 1 ? (u_full - 1) / U * U : 0;
+    static_assert(U <= 6, "the stage loops below are written for 6 stages a round");
+    while (u < u_plain) {
       PKV_PF_STAGE(0, false)
       PKV_PF_STAGE(1, false)
-      if constexpr (PD >= 3) { PKV_PF_STAGE(2, false) }
-      if constexpr (PD >= 4) { PKV_PF_STAGE(3, false) }
+      PKV_PF_STAGE(2, false)
+      if constexpr (U == 6) {
+        PKV_PF_STAGE(3, false)
+        PKV_PF_STAGE(4, false)
+        PKV_PF_STAGE(5, false)
+      }
     }
     for (;;) {
       PKV_PF_STAGE(0, true)
       if (u >= n32) break;
       PKV_PF_STAGE(1, true)
       if (u >= n32) break;
-      if constexpr (PD >= 3) {
-        PKV_PF_STAGE(2, true)
-        if (u >= n32) break;
-      }
-      if constexpr (PD >= 4) {
+      PKV_PF_STAGE(2, true)
+      if (u >= n32) break;
+      if constexpr (U == 6) {
         PKV_PF_STAGE(3, true)
+        if (u >= n32) break;
+        PKV_PF_STAGE(4, true)
+        if (u >= n32) break;
+        PKV_PF_STAGE(5, true)
         if (u >= n32) break;
       }
     }
@@ -1619,7 +1636,7 @@ template <int KIND, int D, int SH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int NR = PrefillCfg<KIND, D>::NR;
-  __shared__ PfStep<KIND, D> kv[PrefillCfg<KIND, D>::PD];
+  __shared__ PfStep<KIND, D> kv[3];
   __shared__ int lct[kPrefillMaxSeqs + 1];
   __shared__ int wsums[4];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
