@@ -46,9 +46,10 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
                 print(" ".join(cmd), flush=True)
             subprocess.run(cmd, check=True)
 
-        kobj = os.path.join(tmp, "kernels.o")
-        run([hipcc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kobj])
-        objs.append(kobj)
+        for name in ("kernels", "prefill"):
+            obj = os.path.join(tmp, name + ".o")
+            run([hipcc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, name + ".hip"), "-o", obj])
+            objs.append(obj)
         cobj = os.path.join(tmp, "capi.o")
         run([hipcc, "-x", "hip", *HIP_FLAGS, "-c", os.path.join(CSRC, "capi.cpp"), "-o", cobj])
         objs.append(cobj)
