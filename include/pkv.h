@@ -322,9 +322,11 @@ pkv_status pkv_decode_attention_merge(const pkv_decode_params* p, void* out,
  * query_start: device int32 [num_seqs + 1], non-decreasing, query_start[0]
  * = 0 and query_start[num_seqs] = num_query_tokens (not checked: it lives
  * on the device).  Other fields, dtypes and limits as pkv_decode_params;
- * num_seqs <= 1024.  No workspace: every (kv head, sequence, tile of
- * 16 / G query tokens) is one wave that walks the table up to its last
- * row's position. */
+ * num_seqs <= 1024; scale may be any finite number (negative and zero
+ * included).  No workspace: a workgroup takes a (kv head, sequence, run of
+ * query tokens) and walks the table up to its last row's position.
+ * Rounding: bf16 and fp8 caches multiply bf16-rounded weights into V and
+ * normalise by the fp32 sum of the weights. */
 typedef struct {
   int32_t num_seqs;
   int32_t num_q_heads;

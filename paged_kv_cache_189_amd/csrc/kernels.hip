@@ -331,11 +331,11 @@ struct RunState {
 };
 
 // Scores, online softmax and P.V for tile b (16 tokens) of the sequence.  L:
-// tokens the lane's query row may see (per lane for causal prefill rows);
-// Lv: tokens of the sequence (wave-uniform).  Scores past L get weight 0;
-// V rows past Lv may hold anything (NaN too) and are selected away.  In the
-// P.V product a lane holds V of dimension r, not query row r, so V masking
-// uses the sequence bound only.
+// tokens the lane's query row may see; Lv: tokens of the sequence (wave-
+// uniform; decode passes the same length for both).  Scores past L get
+// weight 0; V rows past Lv may hold anything (NaN too) and are selected away.
+// In the P.V product a lane holds V of dimension r, not query row r, so V
+// masking uses the sequence bound only.
 template <int KIND, int D>
 __device__ __forceinline__ void process_block(RunState<KIND, D>& st, const Frags<KIND, D>& f,
                                               const QLds<KIND, D>& q, int b, int L, int Lv,
