@@ -263,9 +263,11 @@ typedef struct {
 
 /* Bytes of device workspace pkv_decode_attention needs for these params
  * (0 only for invalid params).  The workspace holds the plan built on the
- * device from context_lens (block prefix sums) and the fp32 partial states
- * (o, m, l, e) of split pieces; its size depends on the params, not on
- * context_lens.  It need not be initialised; it must be 256-byte aligned.
+ * device from context_lens (block prefix sums) and the partial states
+ * (o, m, l, e) of split pieces -- m, l, e in fp32; o in fp32 for fp32
+ * outputs, otherwise bf16 and divided by its own l.  Its size depends on
+ * the params, not on context_lens.  It need not be initialised; it must be
+ * 256-byte aligned.
  * Calls that share a workspace must be ordered on one stream. */
 size_t pkv_decode_workspace_bytes(const pkv_decode_params* p);
 
@@ -285,7 +287,7 @@ pkv_status pkv_decode_attention(const pkv_decode_params* p, void* out, const voi
 /* Pass 1 alone: one kernel whose resident waves each attend to an equal
  * range of the batch's blocks.  A (sequence, kv head) whose pieces all fall
  * to one workgroup (and, with partition cuts, to one partition) gets its
- * final out / lse here; the others leave fp32 partial states in the
+ * final out / lse here; the others leave partial states in the
  * workspace for pass 2 (and empty sequences are left to pass 2).  Up to
  * 1024 sequences the plan is built inside the kernel; larger batches add a
  * one-workgroup planning kernel before it. */
@@ -296,7 +298,8 @@ pkv_status pkv_decode_attention_partitions(const pkv_decode_params* p, void* out
                                            size_t workspace_bytes, float* lse_out, void* stream);
 
 /* Pass 2 alone: merges the partial states pass 1 left: M = max_p m_p,
- * Lambda = sum_p l_p e^{m_p - M}, out = sum_p e^{m_p - M} o_p / Lambda,
+ * Lambda = sum_p l_p e^{m_p - M}, out = sum_p e^{m_p - M} o_p / Lambda
+ * (o_p = l_p times the stored row where rows are stored normalised),
  * lse = M + ln Lambda; also writes the zero rows of empty sequences.  Must
  * follow pass 1 of the same params, inputs and workspace on the same stream,
  * on the same device (the range count depends on the device). */

@@ -408,11 +408,42 @@ struct FoldLds {
 // (the same pair's piece in the next range) and merge it in.  publish >= 0:
 // instead of writing, hand the state to the previous range's wave through
 // fold[publish] and raise flag[publish].
+// Partial O^T rows of a segment slot in the workspace, row major
+// [slot][G][D]: element (slot, head row r, dims nt*16 ..).  The fp32 path
+// keeps sum_t e^{s_t - m} v_t in fp32.  Where the output is bf16 the row is
+// stored normalised by its own weight sum l, in bf16 (round to nearest even):
+// half the bytes pass 1 writes among its reads (partition cuts of long
+// contexts write one row set per partition), and a row of constant V stays
+// exactly that constant through the merge.
+__device__ __forceinline__ int64_t ws_o_at(int64_t slot, int nt, int G, int r, int D) {
+  return ((int64_t)slot * G + r) * D + nt * 16;
+}
+
+// Write lane (r, q4)'s part of partial row (slot, r): O^T[nt*16 + 4 q4 + i].
+template <int KIND, int D>
+__device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t slot, int G, int r,
+                                              int q4, const f32x4 (&o)[Tile<KIND, D>::NT],
+                                              float l_run) {
+  const float f = KIND == kF32 ? a.v_scale : (l_run > 0.f ? a.v_scale / l_run : 0.f);
+#pragma unroll
+  for (int nt = 0; nt < Tile<KIND, D>::NT; ++nt) {
+    const f32x4 v = o[nt] * f;
+    if constexpr (KIND == kF32) {
+      *reinterpret_cast<f32x4*>(a.ws_o + ws_o_at(slot, nt, G, r, D) + 4 * q4) = v;
+    } else {
+      const bf16x2 lo = __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2);
+      const bf16x2 hi = __builtin_convertvector(f32x2{v[2], v[3]}, bf16x2);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.ws_o) + ws_o_at(slot, nt, G, r, D) + 4 * q4) =
+          u32x2{bitcast<uint32_t>(lo), bitcast<uint32_t>(hi)};
+    }
+  }
+}
+
 template <int KIND, int D, int S, int SH>
 __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D>& qs,
                                                FoldLds<KIND, D>* fold, int* flag, int s, int g,
                                                int b_begin, int b_end, int slot, int done,
-                                               int total, int absorb, int publish) {
+                                               int total, int absorb, int publish, int pb) {
   static_assert(S >= 2 && S <= 4, "2 to 4 register buffers");
   using T = Tile<KIND, D>;
   constexpr int NW = 1;  // blocks of the segment are taken in order by this wave
@@ -471,6 +502,26 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
   // loads and the waits stay partial.
   RunState<KIND, D> st;
   st.init();
+  // A range may hold several split-KV partitions of the pair: at each
+  // partition boundary inside it the state so far goes out as the partial of
+  // that partition (slot, slot + 1, ...) and a fresh state starts, while the
+  // loads of the next tiles, already in flight, keep streaming.
+  int to_cut = pb > 0 ? pb - b_begin % pb : 0x7fffffff;
+  auto cut = [&]() {
+    const float l_run = sum_across_groups(st.l);
+    const float e_run = sum_across_groups(st.e);
+    if (r < G) {
+      const int64_t pr = (int64_t)slot * G + r;
+      store_partial<KIND, D>(a, slot, G, r, q4, st.acc.o, l_run);
+      if (q4 == 0) {
+        a.ws_m[pr] = st.m;
+        a.ws_l[pr] = l_run;
+        a.ws_e[pr] = e_run;
+      }
+    }
+    ++slot;
+    st.init();
+  };
   int b = b_begin;
   if (b < b_end) {
     Frags<KIND, D> f0, f1, f2, f3;
@@ -483,7 +534,11 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
   process_block<KIND, D>(st, CUR, qs, b, L, L, a.score_scale_log2, lane, q4); \
   pace(done + (b - b_begin), total);                                     \
   b += NW;                                                               \
-  if (b >= b_end) break;
+  if (b >= b_end) break;                                                 \
+  if (--to_cut == 0) {                                                   \
+    cut();                                                               \
+    to_cut = pb;                                                         \
+  }
     PKV_PREFETCH(f0, 0)
     if constexpr (S >= 3) { PKV_PREFETCH(f1, 1) }
     if constexpr (S >= 4) { PKV_PREFETCH(f2, 2) }
@@ -552,9 +607,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
     if (q4 == 0 && a.lse) a.lse[row] = e_run > 0.f ? (m_run + __builtin_amdgcn_logf(e_run)) * kLn2 : -INFINITY;
   } else {
     const int64_t pr = (int64_t)slot * G + r;
-#pragma unroll
-    for (int nt = 0; nt < T::NT; ++nt)
-      __builtin_nontemporal_store(o[nt] * a.v_scale, reinterpret_cast<f32x4*>(a.ws_o + pr * D + nt * 16 + 4 * q4));
+    store_partial<KIND, D>(a, slot, G, r, q4, st.acc.o, l_run);
     if (q4 == 0) {
       a.ws_m[pr] = m_run;
       a.ws_l[pr] = l_run;
@@ -746,9 +799,8 @@ void decode_partitions_kernel(DecodeArgs a) {
       continue;
     }
     const int lo = (int)(x - ps);
-    const int pidx = pb > 0 ? lo / pb : 0;
-    int hi = pb > 0 ? (pidx + 1) * pb : nblk;
-    hi = hi < nblk ? hi : nblk;
+    const int pidx = pb > 0 ? lo / pb : 0;  // first partition of the segment
+    int hi = nblk;  // the segment runs to the pair's or the range's end
     hi = (int64_t)hi < x1 - ps ? hi : (int)(x1 - ps);
     // Folding: a pair's pieces in the ranges of one workgroup are merged in
     // LDS into the leftmost one, which alone writes (the final row when the
@@ -760,11 +812,12 @@ void decode_partitions_kernel(DecodeArgs a) {
     const int64_t pe = ps + nblk;
     const bool publish = fold_on && x == x_first && lo > 0 && w != 0;
     const bool absorb = fold_on && ps + hi == x1 && hi < nblk && w != NW - 1;
-    const bool whole = fold_on ? lo == 0 && range_of(pe - 1, total, R) / NW == rg / NW : lo == 0 && hi == nblk;
+    const bool whole = fold_on ? lo == 0 && range_of(pe - 1, total, R) / NW == rg / NW
+                               : lo == 0 && hi == nblk && (pb == 0 || nblk <= pb);
     const int slot = g * PT + cp(s) + pidx + rg;
     decode_segment<KIND, D, S, SH>(a, qs[w], fold, flag, s, g, lo, hi, whole ? -1 : slot,
                                (int)(x - x_first), (int)(x1 - x_first), absorb ? w : -1,
-                               publish ? w - 1 : -1);
+                               publish ? w - 1 : -1, pb);
     x = ps + hi;
   }
 }
@@ -841,6 +894,32 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // The segments are listed in LDS with their factors 2^{m_p - M}; the waves
 // then take every fourth entry, each lane D/64 output dimensions, and the
 // four partial sums are added in LDS.
+// Lane `lane`'s V = D / 64 dims of partial row pr (fp32 or bf16 workspace).
+template <int OUT, int D>
+__device__ __forceinline__ void load_partial(const DecodeArgs& a, int64_t pr, int lane,
+                                             float (&x)[D / 64]) {
+  constexpr int V = D / 64;
+  const int64_t at = pr * D + lane * V;
+  if constexpr (OUT == kF32) {
+    if constexpr (V == 2) {
+      const float2 t = *reinterpret_cast<const float2*>(a.ws_o + at);
+      x[0] = t.x;
+      x[1] = t.y;
+    } else {
+      x[0] = a.ws_o[at];
+    }
+  } else {
+    const uint16_t* w = reinterpret_cast<const uint16_t*>(a.ws_o);
+    if constexpr (V == 2) {
+      const uint32_t t = *reinterpret_cast<const uint32_t*>(w + at);
+      x[0] = __uint_as_float(t << 16);
+      x[1] = __uint_as_float(t & 0xFFFF0000u);
+    } else {
+      x[0] = __uint_as_float((uint32_t)w[at] << 16);
+    }
+  }
+}
+
 template <int OUT, int D>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
   constexpr int V = D / 64;
@@ -905,10 +984,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
         const int64_t pr = (int64_t)slot * G + hh;
         const float m = wm[pr];
         const float c = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-        lam += c * a.ws_l[pr];
+        const float cl = c * a.ws_l[pr];
+        lam += cl;
         ex += c * a.ws_e[pr];
         lslot[off] = slot;
-        lcoef[off] = c;
+        lcoef[off] = OUT == kF32 ? c : cl;  // bf16 rows are normalised by l
         ++off;
       });
     __syncthreads();
@@ -920,14 +1000,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
       for (int u = 0; u < 4; ++u) {
         const int e = j + u * kMergeWaves;
         c[u] = lcoef[e];
-        const float* src = a.ws_o + ((int64_t)lslot[e] * G + hh) * D + lane * V;
-        if constexpr (V == 2) {
-          const float2 t = *reinterpret_cast<const float2*>(src);
-          x[u][0] = t.x;
-          x[u][1] = t.y;
-        } else {
-          x[u][0] = src[0];
-        }
+        load_partial<OUT, D>(a, (int64_t)lslot[e] * G + hh, lane, x[u]);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -936,9 +1009,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
     }
     for (; j < n; j += kMergeWaves) {
       const float cj = lcoef[j];
-      const float* src = a.ws_o + ((int64_t)lslot[j] * G + hh) * D + lane * V;
+      float x[V];
+      load_partial<OUT, D>(a, (int64_t)lslot[j] * G + hh, lane, x);
 #pragma unroll
-      for (int v = 0; v < V; ++v) acc[v] += cj != 0.f ? cj * src[v] : 0.f;
+      for (int v = 0; v < V; ++v) acc[v] += cj != 0.f ? cj * x[v] : 0.f;
     }
   } else {
     // Too many segments to list: each wave walks its share of the items.
@@ -955,10 +1029,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
         const int64_t pr = (int64_t)slot * G + hh;
         const float m = wm[pr];
         if (m == -INFINITY) return;
-        const float c = __builtin_amdgcn_exp2f(m - M);
-        const float* src = a.ws_o + pr * D + lane * V;
+        const float c = __builtin_amdgcn_exp2f(m - M) * (OUT == kF32 ? 1.f : a.ws_l[pr]);
+        float x[V];
+        load_partial<OUT, D>(a, pr, lane, x);
 #pragma unroll
-        for (int v = 0; v < V; ++v) acc[v] += c * src[v];
+        for (int v = 0; v < V; ++v) acc[v] += c * x[v];
       });
   }
   const float Lam = block_sum(lam, red);
