@@ -377,7 +377,7 @@ def test_cow_fork_diverge_and_multi_token_append(cache):
 
 
 # ------------------------------------------------------------------- 32-token blocks
-@pytest.mark.parametrize("cache,D", [(F32, 128), (BF16, 128), (BF16, 64), (E4M3, 128)])
+@pytest.mark.parametrize("cache,D", [(F32, 128), (BF16, 128), (BF16, 64), (E4M3, 128), (E4M3, 64)])
 @pytest.mark.parametrize("part", [0, 64])
 def test_block_size_32(cache, D, part):
     """32-token blocks: one multi-token append + cache write (bit-exact
