@@ -42,6 +42,8 @@ struct PrefillCfg {
   using T = Tile<KIND, D>;
   static constexpr int NR = KIND == kF32 ? 1 : 2;  // query tiles per wave
   static constexpr int PD = 2;                      // 32-token steps in flight per wave
+  static constexpr int NWV = 4;                     // waves per workgroup (4 or 8)
+  static constexpr int HPW = 8 / NWV;               // 16-token tiles of a step each wave loads
   // Each wave loads NL pieces of W bytes per lane of each 16-token K tile and
   // as many of the V tile, so the four waves split a step evenly, unbranched.
   static constexpr int W = T::BYTES / 256 < 16 ? T::BYTES / 256 : 16;
@@ -173,8 +175,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   int Ls = as_const(a.context_lens)[s];
   Ls = Ls < 0 ? 0 : (Ls > a.max_context_len ? a.max_context_len : Ls);
   const int per_wave = NQ * NR;
-  const int ibase = item * 4 * per_wave;               // first chunk token of the item
-  const int ilast = (ibase + 4 * per_wave < C ? ibase + 4 * per_wave : C) - 1;
+  constexpr int NWV = C_::NWV, HPW = C_::HPW;
+  const int ibase = item * NWV * per_wave;             // first chunk token of the item
+  const int ilast = (ibase + NWV * per_wave < C ? ibase + NWV * per_wave : C) - 1;
   const int Lmax = Ls - C + ilast + 1;                  // tokens the item's last row sees
   const int Lmin = Ls - C + ibase + 1;                  // ... and its first row
   const int jbase = ibase + w * per_wave;               // this wave's first token
@@ -221,7 +224,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   int vtok[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const uint32_t t = (uint32_t)(((i * 4 + w) * 64 + lane) * W);
+    const uint32_t t = (uint32_t)(((i * 4 + (w & 3)) * 64 + lane) * W);
     ksrc[i] = ((t >> 8) << (8 + shift)) + (t & 255u);
     kdst[i] = t;
     constexpr uint32_t VR = 16u * T::ES;  // V row bytes of a tile
@@ -251,10 +254,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
 #pragma unroll
     for (int nt = 0; nt < T::NT; ++nt) st[k].acc.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  PT sk[PD][2][NL], sv[PD][2][NL];
-  auto load_slot = [&](PT (&dk)[2][NL], PT (&dv)[2][NL], int u) {
+  // With 8 waves, waves 0-3 load the step's first tile and 4-7 its second.
+  const int h0 = HPW == 2 ? 0 : w >> 2;
+  PT sk[PD][HPW][NL], sv[PD][HPW][NL];
+  auto load_slot = [&](PT (&dk)[HPW][NL], PT (&dv)[HPW][NL], int u) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = h0 + hh;
       int t16 = 2 * u + h;
       t16 = t16 < n16 - 1 ? t16 : n16 - 1;
       int64_t phys = __builtin_amdgcn_readfirstlane(tbl[t16 >> shift]);
@@ -266,23 +272,24 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       // and the items of a (head, sequence) pair run side by side on one XCD.
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        dk[h][i] = *reinterpret_cast<gptr<PT>>(kt + ksrc[i]);
-        dv[h][i] = *reinterpret_cast<gptr<PT>>(vt + vsrc[i]);
+        dk[hh][i] = *reinterpret_cast<gptr<PT>>(kt + ksrc[i]);
+        dv[hh][i] = *reinterpret_cast<gptr<PT>>(vt + vsrc[i]);
       }
     }
   };
   // Publish a step to LDS.  On the step holding the sequence end V elements
   // past Lmax are zeroed: their weights are 0 but the slots may hold NaN.
-  auto store_slot = [&](const PT (&dk)[2][NL], const PT (&dv)[2][NL], PfStep<KIND, D>& dst,
+  auto store_slot = [&](const PT (&dk)[HPW][NL], const PT (&dv)[HPW][NL], PfStep<KIND, D>& dst,
                         int u, bool tail) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int h = h0 + hh;
       char* kb = reinterpret_cast<char*>(dst.k[h]);
       char* vb = reinterpret_cast<char*>(dst.v) + h * T::VB;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        *reinterpret_cast<PT*>(kb + kdst[i]) = dk[h][i];
-        PT v = dv[h][i];
+        *reinterpret_cast<PT*>(kb + kdst[i]) = dk[hh][i];
+        PT v = dv[hh][i];
         if (tail) v = zero_from<T::ES>(v, Lmax - (u * 2 + h) * kBS - vtok[i]);
         const Parts pp = bitcast<Parts>(v);
 #pragma unroll
@@ -518,24 +525,25 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
 // through consecutive items of the same sequences and shares their K/V tiles
 // in its L2.
 template <int KIND, int D, int SH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__((64 * PrefillCfg<KIND, D>::NWV)) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int NR = PrefillCfg<KIND, D>::NR;
   __shared__ PfStep<KIND, D> kv[3];
   __shared__ int lct[kPrefillMaxSeqs + 1];
-  __shared__ int wsums[4];
+  constexpr int NWV = PrefillCfg<KIND, D>::NWV;
+  __shared__ int wsums[NWV];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nseq = a.num_seqs, H = a.num_kv_heads;
-  const int per = a.tokens_per_tile * NR * 4;  // query tokens per item
+  const int per = a.tokens_per_tile * NR * NWV;  // query tokens per item
   {
     const int tid = threadIdx.x;
     int carry = 0;
-    for (int c0 = 0; c0 < nseq; c0 += 256) {
+    for (int c0 = 0; c0 < nseq; c0 += 64 * NWV) {
       const int s = c0 + tid;
       int C = s < nseq ? a.query_start[s + 1] - a.query_start[s] : 0;
       C = C < 0 ? 0 : C;
       int tot;
-      const int e = block_exclusive_scan<4>((C + per - 1) / per, wsums, &tot);
+      const int e = block_exclusive_scan<NWV>((C + per - 1) / per, wsums, &tot);
       if (s < nseq) lct[s] = carry + e;
       carry += tot;
     }
@@ -564,7 +572,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int cache, int D, int64_t num_ro
   // one workgroup per item of 4 * NR query tiles; items <= rows / tokens per
   // item + one partial item per sequence
   const int nr = cache == kF32 ? PrefillCfg<kF32, 128>::NR : PrefillCfg<kBF16, 128>::NR;
-  const int per = a.tokens_per_tile * nr * 4;
+  const int per = a.tokens_per_tile * nr * PrefillCfg<kBF16, 128>::NWV;
   const int64_t items = (num_rows + per - 1) / per + a.num_seqs;
   int64_t groups = (int64_t)a.num_kv_heads * items;
   groups = (groups + 7) / 8 * 8;
@@ -572,7 +580,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int cache, int D, int64_t num_ro
     *supported = false;
     return hipSuccess;
   }
-  const dim3 grid((unsigned)groups), block(256);
+  const dim3 grid((unsigned)groups), block(64 * PrefillCfg<kBF16, 128>::NWV);
 #define PKV_PF(C_, D_, SH_)                                                           \
   if (cache == C_ && D == D_ && a.block_shift == SH_) {                               \
     hipLaunchKernelGGL((prefill_kernel<C_, D_, SH_>), grid, block, 0, stream, a);     \
