@@ -13,7 +13,9 @@ next token, so contexts grow by one per step.
 
 Prints one JSON line.  `value` is KV GB/s over the whole step (algorithmic
 KV bytes / step time); `roofline` is the pass-1 kernel's algorithmic bytes
-per launch over its HIP-event-timed average duration, against 8 TB/s.
+per launch over its HIP-event-timed average duration, against 8 TB/s.  The
+events bracket pass 1 on every fifth timed step (at least ten launches): an
+event pair costs ~6 us of step time, which the other steps do not pay.
 """
 from __future__ import annotations
 
@@ -228,10 +230,14 @@ def main():
     torch.cuda.synchronize()
     build_s = time.perf_counter() - t_build
 
-    lens_per_step = []
-    ev = []
+    lens_per_step = []  # every timed step
+    ev, ev_lens = [], []  # the event-timed pass-1 launches and their lengths
+
+    # pass 1 is bracketed by events on every EVENT_EVERY-th timed step
+    event_every = max(1, min(5, args.steps // 10))
 
     def step(i, timed):
+        sampled = timed and (i - args.warmup) % event_every == 0
         buf = pin[i % 2]
         copied[i % 2].synchronize()  # the copy that last read this buffer is done
         sl, ln = buf["slots"].numpy(), buf["lens"].numpy()
@@ -255,14 +261,16 @@ def main():
             d_tables.view(-1).index_put_((d_upd_idx[:n_upd],), d_upd_val[:n_upd])
         pkv.pkv_reshape_and_cache(w.k_new, w.v_new, w.k_cache, w.v_cache, d_slots,  # a2
                                   w.k_scale, w.v_scale)
-        if timed:
+        if sampled:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
         pkv.pkv_decode_attention_partitions(params, out, w.q, w.k_cache, w.v_cache, d_tables,
                                             d_lens, ws, lse)                     # a3-a6, a8
-        if timed:
+        if sampled:
             e1.record(stream)
             ev.append((e0, e1))
+            ev_lens.append(ln.copy())
+        if timed:
             lens_per_step.append(ln.copy())
         pkv.pkv_decode_attention_merge(params, out, d_lens, ws, lse)             # a7
 
@@ -283,14 +291,14 @@ def main():
     # the device tables kept by scattered updates must equal the manager's
     assert np.array_equal(d_tables.cpu().numpy(), tables_now), "device block tables drifted"
     assert np.array_equal(lens_now, host_lens), "context lengths drifted"
-    kv_u, kv_l, oth = [], [], []
+    kv_u, kv_l = [], []
     for ln in lens_per_step:
         u, l = kv_bytes(spec, tables_now, ln)
         kv_u.append(u)
         kv_l.append(l)
-        oth.append(other_bytes(spec, ln))
     kv_step = float(np.mean(kv_u))
-    pass1_bytes = float(np.mean(np.array(kv_u) + np.array(oth)))
+    pass1_bytes = float(np.mean([kv_bytes(spec, tables_now, ln)[0] + other_bytes(spec, ln)
+                                 for ln in ev_lens]))
     achieved = pass1_bytes / (pass1_avg_ms * 1e-3) / 1e9
     value = kv_step / (ms_per_step * 1e-3) / 1e9
     seq_tok_s = S / (ms_per_step * 1e-3)
@@ -315,7 +323,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_partitions_kernel (pass 1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": int(pass1_bytes), "avg_launch_us": round(pass1_avg_ms * 1e3, 2)},
+                     "bytes_per_launch": int(pass1_bytes), "avg_launch_us": round(pass1_avg_ms * 1e3, 2),
+                     "timed_launches": len(ev)},
         "setup_s": round(build_s, 1),
     }
 
