@@ -1281,6 +1281,128 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   if (tid == 0 && a.lse) a.lse[row] = Ex > 0.f ? (M + __builtin_amdgcn_logf(Ex)) * kLn2 : -INFINITY;
 }
 
+// Without partition cuts, the segments of a (sequence, kv head) pair are
+// its pieces in the ranges r_lo .. r_hi it touches, the piece of range r in
+// slot k0 + r.  With folding, a piece starting at a range that is not first
+// in its pass-1 workgroup was merged in pass 1 and holds nothing; without
+// folding (some range is empty) only non-empty ranges own a piece.  So the
+// slots follow from the range indices alone and no list is built: one wave
+// per (sequence, query head) row, four rows per workgroup, reductions inside
+// the wave and no barrier.  Each lane carries one piece's factors; the rows
+// are then summed four at a time, lane = D/64 output dimensions.
+constexpr int kMergeRowsPerGroup = 4;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) v = fmaxf(v, __shfl_xor(v, k));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k);
+  return v;
+}
+
+template <int OUT, int D>
+__global__ __launch_bounds__(64 * kMergeRowsPerGroup) void decode_merge_rows_kernel(DecodeArgs a) {
+  constexpr int V = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int S = a.num_seqs, H = a.num_kv_heads, R = a.num_ranges, Hq = a.num_q_heads;
+  const int row = blockIdx.x * kMergeRowsPerGroup + (int)(threadIdx.x >> 6);  // s * Hq + h
+  if (row >= S * Hq) return;
+  const int s = row / Hq, h = row % Hq;
+  const int G = a.group;
+  const int g = h / G, hh = h % G;
+  const cptr<int32_t> cb = as_const(a.cum);
+  const cptr<int32_t> cp = as_const(a.cum_parts);
+  const int T = cb[S], PT = cp[S];
+  const int c0 = cb[s];
+  const int nblk = cb[s + 1] - c0;
+  if (nblk == 0) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      if constexpr (OUT == kF32)
+        static_cast<float*>(a.out)[(int64_t)row * D + lane * V + v] = 0.f;
+      else
+        static_cast<uint16_t*>(a.out)[(int64_t)row * D + lane * V + v] = 0;
+    }
+    if (lane == 0 && a.lse) a.lse[row] = -INFINITY;
+    return;
+  }
+  const int64_t total = (int64_t)T * H;
+  const int64_t ps = (int64_t)g * T + c0;
+  const int r_lo = range_of(ps, total, R);
+  const int r_hi = range_of(ps + nblk - 1, total, R);
+  const bool fold = total >= R;
+  // finished in pass 1
+  if (fold ? r_lo / kWavesPerGroup == r_hi / kWavesPerGroup : r_lo == r_hi) return;
+  const int k0 = g * PT + cp[s];
+  auto owns = [&](int r) {
+    return r == r_lo || (fold ? r % kWavesPerGroup == 0
+                              : range_start(r + 1, total, R) > range_start(r, total, R));
+  };
+  const int nr = r_hi - r_lo + 1;
+  float mx = -INFINITY;
+  for (int i = lane; i < nr; i += 64)
+    if (owns(r_lo + i)) mx = fmaxf(mx, a.ws_m[(int64_t)(k0 + r_lo + i) * G + hh]);
+  const float M = wave_max(mx);
+  float lam = 0.f, ex = 0.f;
+  float acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  for (int i0 = 0; i0 < nr; i0 += 64) {
+    const int r = r_lo + i0 + lane;
+    const bool mine = i0 + lane < nr && owns(r);
+    const int slot = k0 + r;
+    float coef = 0.f;
+    if (mine) {
+      const int64_t pr = (int64_t)slot * G + hh;
+      const float m = a.ws_m[pr];
+      const float c = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      const float cl = c * a.ws_l[pr];
+      lam += cl;
+      ex += c * a.ws_e[pr];
+      coef = OUT == kF32 ? c : cl;  // bf16 rows are normalised by l
+    }
+    uint64_t left = __ballot(mine);
+    while (left) {
+      int js[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        js[u] = left ? __builtin_ctzll(left) : -1;
+        left &= left - 1;
+      }
+      float x[4][V], cs[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (js[u] >= 0) {
+          cs[u] = __shfl(coef, js[u]);
+          load_partial<OUT, D>(a, (int64_t)__shfl(slot, js[u]) * G + hh, lane, x[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (js[u] >= 0)
+#pragma unroll
+          for (int v = 0; v < V; ++v) acc[v] += cs[u] != 0.f ? cs[u] * x[u][v] : 0.f;
+    }
+  }
+  const float Lam = wave_sum(lam);
+  const float Ex = wave_sum(ex);
+  if constexpr (OUT == kF32) {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      static_cast<float*>(a.out)[(int64_t)row * D + lane * V + v] = Lam > 0.f ? acc[v] / Lam : 0.f;
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      static_cast<uint16_t*>(a.out)[(int64_t)row * D + lane * V + v] =
+          f32_to_bf16_rne(Lam > 0.f ? acc[v] / Lam : 0.f);
+  }
+  if (lane == 0 && a.lse) a.lse[row] = Ex > 0.f ? (M + __builtin_amdgcn_logf(Ex)) * kLn2 : -INFINITY;
+}
+
 // Register buffers (prefetch depth + 1) per cache dtype, at two waves per
 // SIMD (eight per CU).  Three measured the same as two buffers at three
 // waves per SIMD, and leave registers for the fold merge.
@@ -1431,10 +1553,18 @@ hipError_t launch_decode_merge(const DecodeArgs& a, int out, int D, hipStream_t 
                                bool* supported) {
   *supported = true;
   if (a.num_seqs == 0) return hipSuccess;
-  dim3 grid(a.num_seqs * a.num_q_heads), block(kMergeThreads);
+  const int64_t rows = (int64_t)a.num_seqs * a.num_q_heads;
+  // Without partition cuts a row has few segments: one wave per row.  With
+  // them (hundreds of partitions per row) four waves share a row.
+  const bool by_rows = a.part_blocks == 0;
+  dim3 grid(by_rows ? (rows + kMergeRowsPerGroup - 1) / kMergeRowsPerGroup : rows);
+  dim3 block(by_rows ? 64 * kMergeRowsPerGroup : kMergeThreads);
 #define PKV_P2(O_, D_)                                                                      \
   if (out == O_ && D == D_) {                                                               \
-    hipLaunchKernelGGL((decode_merge_kernel<O_, D_>), grid, block, 0, stream, a);           \
+    if (by_rows)                                                                            \
+      hipLaunchKernelGGL((decode_merge_rows_kernel<O_, D_>), grid, block, 0, stream, a);    \
+    else                                                                                    \
+      hipLaunchKernelGGL((decode_merge_kernel<O_, D_>), grid, block, 0, stream, a);         \
     return hipGetLastError();                                                               \
   }
   PKV_P2(kF32, 64) PKV_P2(kF32, 128) PKV_P2(kBF16, 64) PKV_P2(kBF16, 128)
