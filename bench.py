@@ -3,9 +3,10 @@
 One step = one decode step of one attention layer over a batch of resident
 sequences, i.e. the whole hot path:
   a1  host block manager appends one token per sequence (a block is taken
-      only at a block boundary) and exports slots, tables and lengths, which
-      are copied to the device (pinned, double-buffered, async);
-  a2  reshape_and_cache writes each new token's K and V into its slot;
+      only at a block boundary); the slots and lengths are copied to the
+      device (pinned, double-buffered, async);
+  a2  the decode append writes each new token's K and V into its slot and
+      sets the sequence's device table entry for the new position;
   a3-a8  decode attention: pass 1 (per-partition attention over the block
       table) and pass 2 (log-sum-exp merge of split-KV partials).
 Inputs are resident in HBM before the timed region; each step decodes the
@@ -195,24 +196,18 @@ def main():
     workloads.poison_unused(w, tables0[:, : w.max_blocks], lens0 - 1)
 
     out_dtype = torch.float32 if spec.out_dtype == workloads.F32 else torch.bfloat16
-    # Device block tables are copied once; afterwards a step sends its slots,
-    # lengths and the table entries that changed (a sequence starting a new
-    # block) in one small packed buffer, and the entries are scattered on the
-    # device.
+    # Device block tables are copied once; afterwards a step sends its slots
+    # and lengths in one small packed buffer, and the decode append that
+    # writes the new tokens' K/V also sets each sequence's table entry for
+    # its new position (a fresh block at a block boundary).
     d_tables = torch.from_numpy(tables0).to(dev)
-    meta_bytes = 8 * S + 4 * S + 8 * S + 4 * S
+    meta_bytes = 8 * S + 4 * S
 
     def views(buf):
-        o = 0
-        out = []
-        for n, dt in ((8 * S, torch.int64), (4 * S, torch.int32), (8 * S, torch.int64),
-                      (4 * S, torch.int32)):
-            out.append(buf[o:o + n].view(dt))
-            o += n
-        return out
+        return buf[:8 * S].view(torch.int64), buf[8 * S:12 * S].view(torch.int32)
 
     d_meta = torch.empty(meta_bytes, dtype=torch.uint8, device=dev)
-    d_slots, d_lens, d_upd_idx, d_upd_val = views(d_meta)
+    d_slots, d_lens = views(d_meta)
     params = pkv.make_decode_params(w.q, w.k_cache, d_tables, max_blocks * BS, w.scale, w.k_scale,
                                     w.v_scale, out_dtype, part)
     ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(params), 256), dtype=torch.uint8, device=dev)
@@ -222,8 +217,8 @@ def main():
     pin = []
     for _ in range(2):
         hb = torch.empty(meta_bytes, dtype=torch.uint8, pin_memory=True)
-        hs, hl, hi, hv = views(hb)
-        pin.append(dict(raw=hb, slots=hs, lens=hl, upd_idx=hi, upd_val=hv))
+        hs, hl = views(hb)
+        pin.append(dict(raw=hb, slots=hs, lens=hl))
     host_lens = blens.astype(np.int32).copy()
     copied = [torch.cuda.Event(), torch.cuda.Event()]
     stream = torch.cuda.current_stream(dev)
@@ -241,26 +236,17 @@ def main():
         buf = pin[i % 2]
         copied[i % 2].synchronize()  # the copy that last read this buffer is done
         sl, ln = buf["slots"].numpy(), buf["lens"].numpy()
-        n_upd = 0
         if i == 0:
             sl[:], ln[:] = slots0, host_lens
         else:
             rc, _ = bm.append_slots(ids, out=sl)                       # a1
             assert rc == 0, rc
-            pos = host_lens                       # position of each new token
-            new = np.nonzero(pos % BS == 0)[0]    # sequences that took a block
-            n_upd = len(new)
-            if n_upd:
-                buf["upd_idx"].numpy()[:n_upd] = new * max_blocks + pos[new] // BS
-                buf["upd_val"].numpy()[:n_upd] = sl[new] // BS
-            host_lens[:] = pos + 1
+            host_lens[:] += 1
             ln[:] = host_lens
         d_meta.copy_(buf["raw"], non_blocking=True)
         copied[i % 2].record(stream)
-        if n_upd:
-            d_tables.view(-1).index_put_((d_upd_idx[:n_upd],), d_upd_val[:n_upd])
-        pkv.pkv_reshape_and_cache(w.k_new, w.v_new, w.k_cache, w.v_cache, d_slots,  # a2
-                                  w.k_scale, w.v_scale)
+        pkv.pkv_append_decode_tokens(w.k_new, w.v_new, w.k_cache, w.v_cache, d_slots,  # a2
+                                     d_lens, d_tables, w.k_scale, w.v_scale)
         if sampled:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -288,7 +274,7 @@ def main():
 
     # algorithmic bytes, step by step (contexts grow by one token per step)
     _, tables_now, lens_now = bm.export(ids)
-    # the device tables kept by scattered updates must equal the manager's
+    # the device tables kept by the decode append must equal the manager's
     assert np.array_equal(d_tables.cpu().numpy(), tables_now), "device block tables drifted"
     assert np.array_equal(lens_now, host_lens), "context lengths drifted"
     kv_u, kv_l = [], []

@@ -203,6 +203,31 @@ pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype
                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                  int64_t num_blocks, float k_scale, float v_scale, void* stream);
 
+/* Decode-step append on the device: the cache write above for one new token
+ * per sequence, which also keeps a device copy of the block tables in step
+ * with the host block manager ([P1] "PagedAttention Mechanics": appending a
+ * token takes a fresh page only at a page boundary; [P4] section 2: the
+ * kernel finds a token's page through the block table).  Token i is sequence
+ * i's newest token, at position p = context_lens[i] - 1 (context_lens already
+ * counts it); besides writing its K and V into slot_mapping[i] as
+ * pkv_reshape_and_cache does, it sets
+ *   block_tables[i * max_blocks_per_seq + p / block_size] = slot_mapping[i] / block_size,
+ * which is the entry the block manager exports (a new block at a block
+ * boundary, or the copy a copy-on-write gave the sequence).  A token with a
+ * skipped slot, or with p < 0 or p / block_size >= max_blocks_per_seq,
+ * leaves its table row alone.  k_new, v_new: [num_seqs][num_kv_heads][head_dim];
+ * context_lens [num_seqs] int32 and block_tables [num_seqs][max_blocks_per_seq]
+ * int32 are device memory (block_tables is written).  Errors as
+ * pkv_reshape_and_cache, plus PKV_ERR_INVALID_ARG for NULL tables or lengths
+ * or max_blocks_per_seq <= 0. */
+pkv_status pkv_append_decode_tokens(const void* k_new, const void* v_new, pkv_dtype src_dtype,
+                                    void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                                    const int64_t* slot_mapping, const int32_t* context_lens,
+                                    int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_blocks, float k_scale,
+                                    float v_scale, void* stream);
+
 /* Copies whole physical blocks (K and V, every kv head, all block_size
  * slots, bit for bit): block dst[i] <- block src[i] for i < n, e.g. the
  * copy-on-write pairs of pkv_bm_append_slots_cow.  src, dst: device int32

@@ -35,7 +35,8 @@ EXPORTED = (
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_add_seq", "pkv_bm_fork_seq",
     "pkv_bm_append_slots", "pkv_bm_append_slots_cow", "pkv_bm_add_seq_prompt",
     "pkv_bm_append_tokens", "pkv_bm_num_cached_blocks", "pkv_bm_free_seq", "pkv_bm_export",
-    "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_reshape_and_cache", "pkv_copy_blocks",
+    "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_reshape_and_cache",
+    "pkv_append_decode_tokens", "pkv_copy_blocks",
     "pkv_decode_workspace_bytes",
     "pkv_decode_partition_size", "pkv_decode_attention", "pkv_decode_attention_partitions",
     "pkv_decode_attention_merge", "pkv_prefill_attention", "pkv_sim_run", "pkv_status_string",
@@ -117,6 +118,8 @@ def lib():
             "pkv_bm_num_free_blocks": (I32, [P]),
             "pkv_bm_refcount": (I32, [P, I32]),
             "pkv_reshape_and_cache": (st, [P, P, st, P, P, st, P, I32, I32, I32, I32, I64, F, F, P]),
+            "pkv_append_decode_tokens": (st, [P, P, st, P, P, st, P, P, P, I32, I32, I32, I32, I32,
+                                              I64, F, F, P]),
             "pkv_copy_blocks": (st, [P, P, st, P, P, I32, I32, I32, I32, I64, P]),
             "pkv_decode_workspace_bytes": (C.c_size_t, [C.POINTER(pkv_decode_params)]),
             "pkv_decode_partition_size": (I32, [C.POINTER(pkv_decode_params)]),
@@ -289,6 +292,23 @@ def pkv_reshape_and_cache(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: tor
         _ptr(k_new), _ptr(v_new), dtype_code(k_new.dtype), _ptr(k_cache), _ptr(v_cache),
         dtype_code(k_cache.dtype), _ptr(slot_mapping), T, Hkv, D, k_cache.shape[3], k_cache.shape[0],
         float(k_scale), float(v_scale), _stream(stream, k_cache)), "pkv_reshape_and_cache")
+
+
+def pkv_append_decode_tokens(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                             v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                             context_lens: torch.Tensor, block_tables: torch.Tensor,
+                             k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+    """Decode append: k_new, v_new [S][Hkv][D] (token i = sequence i's newest,
+    at position context_lens[i] - 1); writes them into their slots and sets
+    block_tables[i][(context_lens[i] - 1) // block_size] = slot_mapping[i] // block_size."""
+    S, Hkv, D = k_new.shape
+    if block_tables.dim() != 2 or block_tables.shape[0] < S:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    _check(lib().pkv_append_decode_tokens(
+        _ptr(k_new), _ptr(v_new), dtype_code(k_new.dtype), _ptr(k_cache), _ptr(v_cache),
+        dtype_code(k_cache.dtype), _ptr(slot_mapping), _ptr(context_lens), _ptr(block_tables),
+        block_tables.shape[1], S, Hkv, D, k_cache.shape[3], k_cache.shape[0], float(k_scale),
+        float(v_scale), _stream(stream, k_cache)), "pkv_append_decode_tokens")
 
 
 def pkv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor,

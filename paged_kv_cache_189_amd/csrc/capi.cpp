@@ -182,44 +182,75 @@ const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
 const char* pkv_version(void) { return "pkv 0.1 (gfx950)"; }
 
-pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype src_dtype, void* k_cache,
-                                 void* v_cache, pkv_dtype cache_dtype, const int64_t* slot_mapping,
-                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                 int64_t num_blocks, float k_scale, float v_scale, void* stream) {
-  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0)
-    return pkv_fail(PKV_ERR_INVALID_ARG, "reshape_and_cache: bad sizes");
-  if (head_dim != 64 && head_dim != 128)
-    return pkv_fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache: head_dim must be 64 or 128");
-  if (!block_size_ok(block_size)) return pkv_fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache: block_size must be 16 or 32");
+// Shared checks and launch of the cache write; tables / lens / max_blocks
+// only for the decode append.
+static pkv_status cache_write(const char* what, const void* k_new, const void* v_new,
+                              pkv_dtype src_dtype, void* k_cache, void* v_cache,
+                              pkv_dtype cache_dtype, const int64_t* slot_mapping,
+                              const int32_t* context_lens, int32_t* block_tables,
+                              int32_t max_blocks, int32_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                              float k_scale, float v_scale, void* stream) {
+  auto fail = [&](pkv_status st, const char* why) { return pkv_fail(st, std::string(what) + ": " + why); };
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "bad sizes");
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!block_size_ok(block_size)) return fail(PKV_ERR_UNSUPPORTED, "block_size must be 16 or 32");
   const bool combo = (src_dtype == PKV_F32 && (cache_dtype == PKV_F32 || cache_dtype == PKV_BF16 ||
                                                cache_dtype == PKV_FP8_E4M3)) ||
                      (src_dtype == PKV_BF16 && (cache_dtype == PKV_BF16 || cache_dtype == PKV_FP8_E4M3));
-  if (!combo) return pkv_fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache: unsupported (src, cache) dtypes");
+  if (!combo) return fail(PKV_ERR_UNSUPPORTED, "unsupported (src, cache) dtypes");
   if (cache_dtype == PKV_FP8_E4M3 &&
       (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
-    return pkv_fail(PKV_ERR_INVALID_ARG, "reshape_and_cache: fp8 scales must be finite and > 0");
+    return fail(PKV_ERR_INVALID_ARG, "fp8 scales must be finite and > 0");
+  if (block_tables != nullptr && max_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be > 0");
   if (num_tokens == 0) return PKV_OK;
-  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)
-    return pkv_fail(PKV_ERR_INVALID_ARG, "reshape_and_cache: NULL pointer");
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+  if (block_tables != nullptr && context_lens == nullptr) return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(slot_mapping, 8))
-    return pkv_fail(PKV_ERR_INVALID_ARG, "reshape_and_cache: K/V arrays must be 16-byte aligned");
+      !aligned(slot_mapping, 8) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PKV_ERR_INVALID_ARG, "K/V arrays must be 16-byte aligned, slots 8, tables and lengths 4");
   pkv::CacheWriteArgs a;
   a.k_new = k_new;
   a.v_new = v_new;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.slot_mapping = slot_mapping;
+  a.context_lens = context_lens;
+  a.block_tables = block_tables;
   a.num_blocks = num_blocks;
   a.num_tokens = num_tokens;
   a.num_kv_heads = num_kv_heads;
   a.block_size = block_size;
+  a.max_blocks = max_blocks;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   bool ok = false;
   hipError_t e = pkv::launch_cache_write(a, src_dtype, cache_dtype, head_dim, (hipStream_t)stream, &ok);
-  if (!ok) return pkv_fail(PKV_ERR_UNSUPPORTED, "reshape_and_cache: no kernel variant");
-  return check_hip(e, "reshape_and_cache launch");
+  if (!ok) return fail(PKV_ERR_UNSUPPORTED, "no kernel variant");
+  return check_hip(e, (std::string(what) + " launch").c_str());
+}
+
+pkv_status pkv_reshape_and_cache(const void* k_new, const void* v_new, pkv_dtype src_dtype, void* k_cache,
+                                 void* v_cache, pkv_dtype cache_dtype, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int64_t num_blocks, float k_scale, float v_scale, void* stream) {
+  return cache_write("reshape_and_cache", k_new, v_new, src_dtype, k_cache, v_cache, cache_dtype,
+                     slot_mapping, nullptr, nullptr, 0, num_tokens, num_kv_heads, head_dim,
+                     block_size, num_blocks, k_scale, v_scale, stream);
+}
+
+pkv_status pkv_append_decode_tokens(const void* k_new, const void* v_new, pkv_dtype src_dtype,
+                                    void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                                    const int64_t* slot_mapping, const int32_t* context_lens,
+                                    int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_blocks, float k_scale,
+                                    float v_scale, void* stream) {
+  if (num_seqs > 0 && (block_tables == nullptr || context_lens == nullptr))
+    return pkv_fail(PKV_ERR_INVALID_ARG, "append_decode_tokens: NULL pointer");
+  return cache_write("append_decode_tokens", k_new, v_new, src_dtype, k_cache, v_cache, cache_dtype,
+                     slot_mapping, context_lens, block_tables, max_blocks_per_seq, num_seqs,
+                     num_kv_heads, head_dim, block_size, num_blocks, k_scale, v_scale, stream);
 }
 
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype, const int32_t* src,

@@ -73,7 +73,10 @@ __device__ __forceinline__ float load_src(const void* p, int64_t i) {
 // ---------------------------------------------------------------- cache write
 // One workgroup per new token; threads stride over (kv head, 16-byte chunk).
 // With B = block_size: K chunk c of head h goes to block[h][c][slot % B][0..X);
-// V element d goes to block[h][d][slot % B].
+// V element d goes to block[h][d][slot % B].  As a decode append (tables
+// given), token t is sequence t's token at position p = context_lens[t] - 1
+// and entry p / B of its table row is set to the slot's block, the value the
+// host block manager holds there.
 template <int SRC, int CACHE, int D>
 __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
   constexpr int ES = ElemSize<CACHE>::value;
@@ -85,6 +88,10 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
   if (slot < 0 || slot >= a.num_blocks * B) return;
   const int64_t blk = slot / B;
   const int off = (int)(slot % B);
+  if (a.block_tables != nullptr && threadIdx.x == 0) {
+    const int p = a.context_lens[t] - 1;
+    if (p >= 0 && p / B < a.max_blocks) a.block_tables[(int64_t)t * a.max_blocks + p / B] = (int32_t)blk;
+  }
   for (int e = threadIdx.x; e < a.num_kv_heads * CH; e += blockDim.x) {
     const int h = e / CH, c = e % CH;
     const int64_t src0 = ((int64_t)t * a.num_kv_heads + h) * D + c * X;

@@ -75,10 +75,15 @@ struct CacheWriteArgs {
   void* k_cache;
   void* v_cache;
   const int64_t* slot_mapping;
+  // Decode append (optional): token t is sequence t's newest token, at
+  // position context_lens[t] - 1; its table entry is set to its block.
+  const int32_t* context_lens;
+  int32_t* block_tables;  // [num_tokens][max_blocks] or null
   int64_t num_blocks;
   int32_t num_tokens;
   int32_t num_kv_heads;
   int32_t block_size;  // tokens per physical block (16 or 32)
+  int32_t max_blocks;
   float k_scale;
   float v_scale;
 };

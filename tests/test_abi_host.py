@@ -279,3 +279,32 @@ def test_cache_write_validation():
     assert f(24, 16, 1, 16, 16, 1, 16, 1, 8, 128, 16, 10, 1.0, 1.0, None) == pkv.PKV_ERR_INVALID_ARG
     assert f(None, 16, 1, 16, 16, 1, 16, 1, 8, 128, 16, 10, 1.0, 1.0, None) == pkv.PKV_ERR_INVALID_ARG
     assert f(None, None, 1, None, None, 1, None, 0, 8, 128, 16, 10, 1.0, 1.0, None) == 0
+
+
+def test_append_decode_tokens_validation():
+    # fake pointers: every call here must be rejected (or be a no-op) on the host
+    L = pkv.lib()
+    f = L.pkv_append_decode_tokens
+    # (k_new, v_new, src, k_cache, v_cache, cache, slots, lens, tables, max_blocks,
+    #  num_seqs, kv_heads, head_dim, block_size, num_blocks, k_scale, v_scale, stream)
+    ok = (16, 16, 1, 16, 16, 1, 16, 16, 16, 8, 4, 8, 128, 16, 10, 1.0, 1.0, None)
+
+    def call(**kw):
+        args = list(ok)
+        names = ["k", "v", "src", "kc", "vc", "cache", "slots", "lens", "tables", "mb", "n", "h",
+                 "d", "bs", "nb", "ks", "vs", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(tables=None) == pkv.PKV_ERR_INVALID_ARG
+    assert call(lens=None) == pkv.PKV_ERR_INVALID_ARG
+    assert call(mb=0) == pkv.PKV_ERR_INVALID_ARG
+    assert call(tables=18) == pkv.PKV_ERR_INVALID_ARG          # misaligned table
+    assert call(d=96) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(bs=8) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(cache=2, ks=0.0) == pkv.PKV_ERR_INVALID_ARG
+    assert call(n=-1) == pkv.PKV_ERR_INVALID_ARG
+    assert call(n=0, k=None, v=None, kc=None, vc=None, slots=None, lens=None,
+                tables=None) == pkv.PKV_OK
+    assert "append_decode_tokens" in L.pkv_last_error().decode()

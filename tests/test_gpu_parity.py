@@ -608,3 +608,55 @@ def test_prefix_cache_reuses_cached_kv_end_to_end():
                                 float(np.float32(1 / math.sqrt(D))))
     err = np.abs(out.float().cpu().numpy() - ref).max()
     assert err <= G.TOL[BF16], err
+
+
+# ------------------------------------------------------------------- decode append (cache + tables)
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+def test_append_decode_tokens_sets_tables_and_cache(cache):
+    """pkv_append_decode_tokens: the cache bytes equal the oracle's cache
+    write, the device table entry of each new position equals the host block
+    manager's (poisoned beforehand, so a missed write shows), a skipped slot
+    leaves its row alone, and decode over the updated tables matches the oracle."""
+    lens = [1, 16, 17, 33, 100, 257, 1000, 1025]
+    spec = small_spec(960 + cache, 2, len(lens), 16, 4, 128, lens, cache)
+    c = G.build(spec)
+    S = len(c.lens)
+    seqs = np.arange(S)
+    before = G.host_copy(c, seqs)
+    pos = c.lens.astype(np.int64) - 1
+    col = torch.from_numpy(pos // BS).cuda()
+    rows = torch.arange(S, device="cuda")
+    c.d_tables[rows, col] = -7
+    skip = 3
+    slots = c.d_slots.clone()
+    slots[skip] = -1
+    G.log(f"[append decode tokens dtype={cache}] skipped slot of sequence {skip}")
+    w = c.w
+    pkv.pkv_append_decode_tokens(w.k_new, w.v_new, w.k_cache, w.v_cache, slots, c.d_lens,
+                                 c.d_tables, w.k_scale, w.v_scale)
+    torch.cuda.synchronize()
+    got = c.d_tables.cpu().numpy()
+    want = c.tables.copy()
+    want[skip, pos[skip] // BS] = -7
+    assert np.array_equal(got, want), "device tables differ from the block manager's"
+    # the skipped token wrote nothing; then write it and check every byte
+    after_skip = G.host_copy(c, seqs)
+    c.d_tables.copy_(torch.from_numpy(c.tables).cuda())
+    G.log(f"[append decode tokens dtype={cache}] all slots, then decode")
+    pkv.pkv_append_decode_tokens(w.k_new, w.v_new, w.k_cache, w.v_cache, c.d_slots, c.d_lens,
+                                 c.d_tables, w.k_scale, w.v_scale)
+    G.run_decode(c)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.d_tables.cpu().numpy(), c.tables)
+    after = G.host_copy(c, seqs)
+    G.oracle_cache_write(c, before)
+    assert np.array_equal(G.bits(before.k), G.bits(after.k)), "K cache bytes differ"
+    assert np.array_equal(G.bits(before.v), G.bits(after.v)), "V cache bytes differ"
+    # the skipped sequence's block held its old bytes after the first call
+    b_skip = np.searchsorted(before.blocks, int(c.slots_o[skip]) // BS)
+    others = np.ones(len(before.blocks), dtype=bool)
+    others[b_skip] = False
+    assert np.array_equal(G.bits(after_skip.k[others]), G.bits(before.k[others]))
+    assert not np.array_equal(G.bits(after_skip.k[b_skip]), G.bits(before.k[b_skip]))
+    ref, rlse, _ = G.oracle_decode(c, before)
+    G.compare_out(c, seqs, ref, rlse, f"append decode dtype={cache}")
