@@ -415,23 +415,41 @@ __device__ __forceinline__ Offsets32 offsets32(int lane, int r, int q4) {
   return o;
 }
 
+// Two consecutive 16-token blocks A (tokens 0-15) and B (16-31) taken as one
+// 32-token stage: the same MFMA row order, so K lane-row m < 8 and V lanes
+// with q4 < 2 read A, the others B, each at its offset in a 16-token block
+// (K chunk stride 256 bytes, V row 16 * ES bytes).
+template <int KIND, int D>
+__device__ __forceinline__ Offsets32 offsets_pair(int lane, int r, int q4) {
+  Offsets32 o;
+  const uint32_t m = (uint32_t)lane & 15u, cq = (uint32_t)lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) o.koff[h] = cq * 256u + ((8u * (m >> 2) + 4u * h + (m & 3u)) & 15u) * 16u;
+  o.voff = ((uint32_t)r * 16u + 8u * ((uint32_t)q4 & 1u)) * Tile<KIND, D>::ES;
+  return o;
+}
+
 // A block's K chunk j of lane-row cq sits at (4 j + cq) * 512 bytes; V row d
 // at d * 32 * ES bytes.  Every line of the block is read in this stage.
+// (PAIR: a 16-token block pair, K chunk j at (4 j + cq) * 256 bytes and V
+// row d at d * 16 * ES bytes of the lane's block.)
 // Cache policy measured per dtype: fp8 blocks stream (non-temporal, +10% on
 // the 70B-shaped fp8 workload); bf16 blocks keep the default policy, which
 // lets the blocks of a shared prefix stay in L2 for the other sequences
 // (+12% on the shared-prefix workload, within 1% elsewhere).
-template <int KIND, int D, bool STREAM>
+template <int KIND, int D, bool STREAM, bool PAIR = false>
 __device__ __forceinline__ void load_block32(Frags32<KIND, D>& f, gchar_p kt, gchar_p vt,
                                              const Offsets32& o) {
   using T = Tile<KIND, D>;
   using F = Frags32<KIND, D>;
+  constexpr int KJ = PAIR ? 1024 : 2048;                // K bytes per chunk group j
+  constexpr int VNT = (PAIR ? 256 : 512) * T::ES;       // V bytes per 16 dims
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int j = 0; j < T::NK; ++j)
     {
-      gptr<u32x4> pk = reinterpret_cast<gptr<u32x4>>(kt + j * 2048 + o.koff[h]);
+      gptr<u32x4> pk = reinterpret_cast<gptr<u32x4>>(kt + j * KJ + o.koff[h]);
       f.k[h][j] = STREAM ? __builtin_nontemporal_load(pk) : *pk;
     }
 #pragma unroll
@@ -439,7 +457,7 @@ __device__ __forceinline__ void load_block32(Frags32<KIND, D>& f, gchar_p kt, gc
 #pragma unroll
     for (int pc = 0; pc < F::VN; ++pc)
     {
-      gptr<typename F::VP> pv = reinterpret_cast<gptr<typename F::VP>>(vt + nt * 512 * T::ES + o.voff + pc * 16);
+      gptr<typename F::VP> pv = reinterpret_cast<gptr<typename F::VP>>(vt + nt * VNT + o.voff + pc * 16);
       f.v[nt][pc] = STREAM ? __builtin_nontemporal_load(pv) : *pv;
     }
 }
@@ -714,29 +732,46 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
     ++slot;
     st.init();
   };
-  constexpr bool kWhole = SH == 1 && KIND != kF32;  // fp32 blocks would not fit in registers
+  // fp8 16-token blocks are taken two at a time (a 2 KiB K tile per stage
+  // leaves too little work per stage to cover a block's latency).
+  constexpr bool kPair = SH == 0 && KIND == kFP8;
+  constexpr bool kWhole = (SH == 1 && KIND != kF32) || kPair;  // fp32 blocks would not fit in registers
   if constexpr (kWhole) {
-    // 32-token blocks: a stage per block.  The segment's tiles [b_begin,
-    // b_end) may start or end mid-block; those stages mask the other half.
+    // 32-token blocks (or 16-token block pairs): a stage per block.  The
+    // segment's tiles [b_begin, b_end) may start or end mid-block; those
+    // stages mask the other half.
     constexpr int S32 = KIND == kFP8 ? 3 : 2;  // register buffers (blocks)
     static_assert(KIND != kF32, "fp32 32-token blocks take the 16-token tile path");
-    const Offsets32 o32 = offsets32<KIND, D>(lane, r, q4);
+    const Offsets32 o32 = kPair ? offsets_pair<KIND, D>(lane, r, q4) : offsets32<KIND, D>(lane, r, q4);
+    const bool k_from_b = (lane & 15) >= 8, v_from_b = q4 >= 2;  // pair: lanes reading block B
     const int u0 = b_begin >> 1, u1 = (b_end - 1) >> 1;  // blocks, inclusive
     const int tmin = b_begin * kBS, tmax = b_end * kBS < L ? b_end * kBS : L;
     int next_cut = pb > 0 ? (b_begin / pb + 1) * pb : 0x7fffffff;  // in tiles
     int u = u0;
     auto block_of = [&](int ub, gchar_p& kt, gchar_p& vt) {
-      int64_t phys = __builtin_amdgcn_readfirstlane(tbl[ub]);
-      phys = phys < 0 ? 0 : (phys > last_block ? last_block : phys);
-      kt = uniform_ptr(kbase + phys * bstride);
-      vt = uniform_ptr(vbase + phys * bstride);
+      if constexpr (kPair) {
+        // tiles 2 ub and 2 ub + 1; past the segment's last tile B repeats A
+        // (its tokens are masked), so no entry past the segment is read
+        const int ib = 2 * ub + 1 < b_end ? 2 * ub + 1 : 2 * ub;
+        int64_t pa = __builtin_amdgcn_readfirstlane(tbl[2 * ub]);
+        int64_t pbk = __builtin_amdgcn_readfirstlane(tbl[ib]);
+        pa = pa < 0 ? 0 : (pa > last_block ? last_block : pa);
+        pbk = pbk < 0 ? 0 : (pbk > last_block ? last_block : pbk);
+        kt = (gchar_p)(kbase + (k_from_b ? pbk : pa) * bstride);
+        vt = (gchar_p)(vbase + (v_from_b ? pbk : pa) * bstride);
+      } else {
+        int64_t phys = __builtin_amdgcn_readfirstlane(tbl[ub]);
+        phys = phys < 0 ? 0 : (phys > last_block ? last_block : phys);
+        kt = uniform_ptr(kbase + phys * bstride);
+        vt = uniform_ptr(vbase + phys * bstride);
+      }
     };
     if (b_begin < b_end) {
       Frags32<KIND, D> g0, g1, g2;
       gchar_p kt, vt;
 #define PKV_PREFETCH32(BUF, AHEAD)                 \
   block_of(min(u + (AHEAD), u1), kt, vt);          \
-  load_block32<KIND, D, KIND == kFP8>(BUF, kt, vt, o32);
+  load_block32<KIND, D, KIND == kFP8, kPair>(BUF, kt, vt, o32);
 // The next block's loads go out once this block's scores are formed, so its
 // K registers are free to take them: a block and a half in flight.
 #define PKV_STAGE32(CUR, NXT)                                                                 \
