@@ -1,18 +1,21 @@
-"""Kernel statistics and HBM counters of the decode pass-1 kernel.
+"""rocprofv3 evidence for the decode pass-1 kernel and the chunked-prefill kernel.
 
-For each workload this runs `bench.py` three times under rocprofv3 (one
-kernel trace with statistics, one FETCH_SIZE pass, one WRITE_SIZE pass; one
-counter per pass) and, once, a plain 1 GiB device copy under each counter to
-calibrate them.  It writes, under profiles/, one summary per workload and
+For each workload this runs `bench.py` under rocprofv3: one kernel trace with
+statistics, one FETCH_SIZE pass and one WRITE_SIZE pass (one counter per pass),
+then one pass each for the derived metrics LDSBankConflict (percent of GPU time
+the LDS stalls on bank conflicts), MeanOccupancyPerCU (resident waves per CU)
+and VALUBusy + MfmaUtil (percent of time the vector ALU / the matrix cores are
+busy); once, a plain 1 GiB device copy under each byte counter calibrates them.
+It writes one summary per workload under profiles/ and, for decode,
 pass1_hbm_counters.json, which bench.py reads for `roofline.traffic` while the
 decode sources still hash to the value recorded there.
 
 Usage (on a machine with the GPU, from the repository root):
-    python profile_decode.py [--workloads 2:0,3:0,4:0,5:512] [--out gpurun_out/prof]
+    python profile_kernels.py [--decode 2:0,3:0,4:0,5:512] [--prefill 2:512,4:512]
+                              [--out gpurun_out/prof]
 and, where only the --out folder comes back from that machine, again with
---from-output to write the summaries from it.
-rocprofv3 is started as a child process with the Python interpreter right
-after `--`.
+--from-output to write the summaries from it.  rocprofv3 is started as a child
+process with the Python interpreter right after `--`.
 """
 from __future__ import annotations
 
@@ -31,6 +34,10 @@ sys.path.insert(0, ROOT)
 PROFILES = os.path.join(ROOT, "profiles")
 COUNTERS = os.path.join(PROFILES, "pass1_hbm_counters.json")
 KERNEL = "decode_partitions"
+PREFILL_KERNEL = "prefill_kernel"
+# derived-metric passes (each small enough for one hardware pass)
+METRIC_PASSES = (("lds", ("LDSBankConflict",)), ("occ", ("MeanOccupancyPerCU",)),
+                 ("busy", ("VALUBusy", "MfmaUtil")))
 SLUG = {2: "llama3_8b_bf16", 3: "llama31_70b_shared_prefix_bf16", 4: "llama31_70b_fp8_kv",
         5: "llama31_405b_long_context_bf16"}
 COPY_MIB = 1024
@@ -92,6 +99,36 @@ def per_dispatch(d, counter, name_part):
     return list(vals.values())
 
 
+def metric_means(d, names, name_part):
+    """Mean over the dispatches of kernel name_part of each derived metric."""
+    return {m: sum(v) / len(v) for m in names for v in [per_dispatch(d, m, name_part)]}
+
+
+def metric_runs(a, tag, base, kernel, py):
+    """The derived-metric passes of one workload: (commands, {metric: mean})."""
+    cmds, vals = [], {}
+    for ptag, names in METRIC_PASSES:
+        d = f"{a.out}/{tag}/{ptag}"
+        cmd = ["rocprofv3", "--pmc", *names, "--kernel-include-regex", kernel,
+               "--output-format", "csv", "-d", d, "-o", "t"] + base
+        cmds.append(cmd)
+        run(cmd, f"{a.out}/{tag}_{ptag}.log", 120)
+        vals.update(metric_means(d, names, kernel))
+    return cmds, vals
+
+
+def metric_lines(vals, waves_cap):
+    return [
+        "## Occupancy, LDS and ALU counters",
+        "",
+        f"- LDSBankConflict {vals['LDSBankConflict']:.2f}% of GPU time the LDS is stalled on bank conflicts",
+        f"- MeanOccupancyPerCU {vals['MeanOccupancyPerCU']:.2f} resident waves per CU "
+        f"(the launch allows {waves_cap})",
+        f"- VALUBusy {vals['VALUBusy']:.1f}%, MfmaUtil {vals['MfmaUtil']:.1f}% of GPU time",
+        "",
+    ]
+
+
 def short(name, n=88):
     name = name.replace("(anonymous namespace)::", "")
     return name if len(name) <= n else name[:n] + "..."
@@ -106,7 +143,10 @@ def stats_rows(d, top=8):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--workloads", default="2:0,3:0,4:0,5:512")
+    ap.add_argument("--decode", default="2:0,3:0,4:0,5:512",
+                    help="decode workloads, config:partition_tokens")
+    ap.add_argument("--prefill", default="2:512,4:512",
+                    help="prefill workloads, config:chunk_tokens ('' for none)")
     ap.add_argument("--out", default="gpurun_out/prof")
     ap.add_argument("--from-output", action="store_true",
                     help="run nothing: write the summaries from the rocprofv3 output and logs "
@@ -155,7 +195,7 @@ def main():
     })
     doc.setdefault("workloads", {})
 
-    for wl in a.workloads.split(","):
+    for wl in [w for w in a.decode.split(",") if w]:
         cfg, part = (int(x) for x in wl.split(":"))
         tag = f"c{cfg}" + (f"p{part}" if part else "")
         base = ["--", py, "-u", "bench.py", "--config", str(cfg), "--partition", str(part)]
@@ -175,6 +215,8 @@ def main():
             pl = bench_line(run(cmd, f"{a.out}/{tag}_{counter}.log", 300))
             v = per_dispatch(d, counter, KERNEL)
             got[counter] = (sum(v) / len(v), len(v), pl["roofline"]["bytes_per_launch"])
+        mbase = base + ["--steps", "5", "--warmup", "1", "--no-cpu-baseline"]
+        mcmds, mvals = metric_runs(a, tag, mbase, KERNEL, py)
         fetch_kib, nd, alg = got["FETCH_SIZE"]
         write_kib = got["WRITE_SIZE"][0]
         rd = fetch_kib * 1024 * scale["FETCH_SIZE"]
@@ -235,6 +277,11 @@ def main():
             f"- decode sources hash at measurement (sha256 of kernels.hip, device_common.h, "
             f"pkv_launch.h with comments and white space removed): `{sha}`",
             "",
+            *metric_lines(mvals, 8),
+            "```",
+            *[" ".join(c).replace(py, "python") for c in mcmds],
+            "```",
+            "",
         ]
         with open(os.path.join(PROFILES, fname), "w") as f:
             f.write("\n".join(lines))
@@ -243,6 +290,83 @@ def main():
         with open(COUNTERS, "w") as f:
             json.dump(doc, f, indent=1)
             f.write("\n")
+    for wl in [w for w in a.prefill.split(",") if w]:
+        cfg, chunk = (int(x) for x in wl.split(":"))
+        tag = f"pf{cfg}c{chunk}"
+        base = ["--", py, "-u", "bench.py", "--op", "prefill", "--config", str(cfg), "--chunk",
+                str(chunk)]
+        trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+                     f"{a.out}/{tag}/trace", "-o", "t"] + base + [
+                     "--steps", "10", "--warmup", "2", "--no-cpu-baseline"]
+        line = bench_line(run(trace_cmd, f"{a.out}/{tag}_trace.log", 300))
+        rows = stats_rows(f"{a.out}/{tag}/trace")
+        mbase = base + ["--steps", "3", "--warmup", "1", "--no-cpu-baseline"]
+        got, pmc_cmds = {}, []
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            d = f"{a.out}/{tag}/{counter.split('_')[0].lower()}"
+            cmd = ["rocprofv3", "--pmc", counter, "--kernel-include-regex", PREFILL_KERNEL,
+                   "--output-format", "csv", "-d", d, "-o", "t"] + mbase
+            pmc_cmds.append(cmd)
+            run(cmd, f"{a.out}/{tag}_{counter}.log", 300)
+            v = per_dispatch(d, counter, PREFILL_KERNEL)
+            got[counter] = sum(v) / len(v)
+        mcmds, mvals = metric_runs(a, tag, mbase, PREFILL_KERNEL, py)
+        rd = got["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
+        wr = got["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
+        r = line["roofline"]
+        pk = [x for x in rows if PREFILL_KERNEL in x["Name"]]
+        k_us = float(pk[0]["AverageNs"]) / 1e3 if pk else float("nan")
+        name = line["config"]["workload"]
+        fname = f"prefill_kernel_{SLUG[cfg]}_chunk{chunk}.md"
+        lines = [
+            f"# Chunked-prefill kernel on {name}, chunk {chunk}",
+            "",
+            f"Every sequence attends its last {chunk} cached tokens causally over its whole paged "
+            f"context ({line['config']['query_tokens']} query tokens in all).",
+            "",
+            "Kernel statistics (rocprofv3), run from the repository root on one MI355X:",
+            "",
+            "```",
+            " ".join(trace_cmd).replace(py, "python"),
+            "```",
+            "",
+            "| kernel | calls | avg us | min us | max us | % of GPU time |",
+            "|---|---|---|---|---|---|",
+        ]
+        for row in rows:
+            lines.append(f"| `{short(row['Name'])}` | {row['Calls']} | {float(row['AverageNs']) / 1e3:.1f} | "
+                         f"{float(row['MinNs']) / 1e3:.1f} | {float(row['MaxNs']) / 1e3:.1f} | "
+                         f"{float(row['Percentage']):.1f} |")
+        lines += [
+            "",
+            f"Under the profiler the bench line read the kernel at {r['avg_launch_us']} us (HIP "
+            f"events on the launch stream) against {k_us:.1f} us average kernel time above; "
+            f"algorithmic work per launch {r['flops_per_launch'] / 1e12:.4f} TFLOP (4 * D per "
+            f"visible (row, head, token)) -> {r['achieved']} TFLOP/s, {100 * r['frac']:.1f}% of the "
+            f"{r['peak']:.0f} TFLOP/s dense MFMA peak of its compute dtype.",
+            "",
+            "## Fabric traffic of the prefill kernel",
+            "",
+            "```",
+            *[" ".join(c).replace(py, "python") for c in pmc_cmds],
+            "```",
+            "",
+            f"FETCH_SIZE {got['FETCH_SIZE']:.0f} KiB and WRITE_SIZE {got['WRITE_SIZE']:.0f} KiB per "
+            f"dispatch, scaled by the copy calibration (x{scale['FETCH_SIZE']:.3f}, "
+            f"x{scale['WRITE_SIZE']:.3f}): {rd / 1e9:.3f} GB read and {wr / 1e9:.3f} GB written per "
+            f"launch, against {line['kv_bytes'] / 1e9:.3f} GB of unique K/V bytes the chunks see "
+            f"(every query item of a (head, sequence) pair re-reads the context, mostly from L2).",
+            "",
+            *metric_lines(mvals, 8),
+            "```",
+            *[" ".join(c).replace(py, "python") for c in mcmds],
+            "```",
+            "",
+        ]
+        with open(os.path.join(PROFILES, fname), "w") as f:
+            f.write("\n".join(lines))
+        log(f"prefill {cfg}:{chunk}: {k_us:.1f} us, {r['achieved']} TFLOP/s, "
+            f"MfmaUtil {mvals['MfmaUtil']:.1f}% VALUBusy {mvals['VALUBusy']:.1f}% -> profiles/{fname}")
     log("done")
 
 
