@@ -734,9 +734,12 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
   };
   // fp8 16-token blocks are taken two at a time (a 2 KiB K tile per stage
   // leaves too little work per stage to cover a block's latency).
+  // Pairs cut only at even tiles: with an odd number of tiles per partition
+  // the segment takes the 16-token tile loop below instead.
   constexpr bool kPair = SH == 0 && KIND == kFP8;
   constexpr bool kWhole = (SH == 1 && KIND != kF32) || kPair;  // fp32 blocks would not fit in registers
-  if constexpr (kWhole) {
+  const bool whole = kWhole && !(kPair && (pb & 1));
+  if constexpr (kWhole) if (whole) {
     // 32-token blocks (or 16-token block pairs): a stage per block.  The
     // segment's tiles [b_begin, b_end) may start or end mid-block; those
     // stages mask the other half.
@@ -840,7 +843,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
 #undef PKV_STAGE
 #undef PKV_PREFETCH
   };
-  if constexpr (!kWhole) {
+  if (!whole) {
     // The leading tiles of a sequence (where a shared prefix sits) take the
     // default cache policy, so that other sequences reading the same blocks
     // find them in L2; the rest streams with non-temporal loads.

@@ -73,7 +73,7 @@ RAGGED = [1, 15, 16, 17, 100, 511, 512, 513, 1500, 2049]
 
 
 @pytest.mark.parametrize("cache", [F32, BF16, E4M3])
-@pytest.mark.parametrize("part", [0, 64])
+@pytest.mark.parametrize("part", [0, 16, 48, 64])
 def test_ragged_lengths(cache, part):
     base = {F32: 1, BF16: 2, E4M3: 4}[cache]
     spec = small_spec(200 + cache, base, len(RAGGED), 32, 8, 128, RAGGED, cache)
@@ -92,6 +92,22 @@ def test_many_ranges_per_sequence(cache):
     spec = small_spec(210 + cache, base, len(lens), 32, 8, 128, lens, cache)
     c = G.build(spec, partition_size=0)
     full_parity(c, label=f"many ranges dtype={cache}")
+
+
+@pytest.mark.parametrize("cache", [BF16, E4M3])
+@pytest.mark.parametrize("part", [16, 48, 96])
+def test_partition_cuts_odd_and_even_tiles(cache, part):
+    """Partitions of an odd (1, 3) and an even (6) number of 16-token tiles
+    over sequences that span many ranges: the fp8 path takes two blocks per
+    stage only where every cut falls between pairs, and the 16-token tile
+    loop otherwise."""
+    rng = np.random.default_rng(23 + cache + part)
+    lens = np.concatenate([rng.integers(1, 200, 8), rng.integers(200, 3000, 8),
+                           rng.integers(3000, 9000, 6)])
+    base = {BF16: 2, E4M3: 4}[cache]
+    spec = small_spec(230 + cache, base, len(lens), 32, 8, 128, lens, cache)
+    c = G.build(spec, partition_size=part)
+    full_parity(c, label=f"partition cuts dtype={cache} part={part}")
 
 
 @pytest.mark.parametrize("cache", [F32, BF16, E4M3])
