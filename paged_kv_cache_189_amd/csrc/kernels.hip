@@ -162,9 +162,10 @@ struct Frags {
   typename T::V v[T::NT];
 };
 
-// K/V tiles are streamed once per step: non-temporal loads (the nt bit)
+// Most K/V tiles are read once per step: non-temporal loads (the nt bit)
 // keep them from displacing reusable lines in L2 and measured ~12% more
-// read bandwidth on MI355X for randomly placed 4-8 KiB tiles.
+// read bandwidth on MI355X for randomly placed 4-8 KiB tiles.  The leading
+// tiles of each sequence are the exception (HotTiles below).
 // Lane offsets into one 16-token tile of a block of B = 16 << shift tokens:
 // K is [D/X][B][X] per (block, head), so lane l reads 16 bytes of token l % 16
 // in d-chunk 4j + l / 16; V is [D][B], lane (r, q4) reads tokens 4 q4 .. +3 of
