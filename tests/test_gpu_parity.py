@@ -676,3 +676,52 @@ def test_append_decode_tokens_sets_tables_and_cache(cache):
     assert not np.array_equal(G.bits(after_skip.k[b_skip]), G.bits(before.k[b_skip]))
     ref, rlse, _ = G.oracle_decode(c, before)
     G.compare_out(c, seqs, ref, rlse, f"append decode dtype={cache}")
+
+
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+def test_append_decode_tokens_block_size_32(cache):
+    """The decode append over 32-token blocks: contexts are appended on the
+    host, then one decode token per sequence goes through
+    pkv_append_decode_tokens; the pools equal the oracle's cache write bit
+    for bit and the device table equals the block manager's, with entry
+    (L - 1) / 32 poisoned beforehand."""
+    BS32, D, Hkv = 32, 128, 4
+    gen = torch.Generator().manual_seed(130 + cache)
+    lens = np.array([1, 31, 32, 33, 64, 65, 100, 1000], dtype=np.int64)  # after the append
+    nb = int(sum(-(-lens // BS32))) + 5
+    mb = int(-(-lens.max() // BS32)) + 1
+    qd = F32 if cache == F32 else BF16
+    ksc, vsc = (1.0, 1.0) if cache != E4M3 else (0.017, 0.019)
+    order = np.random.default_rng(131 + cache).permutation(nb).astype(np.int32)
+    bm = pkv.BlockManager(nb, BS32, mb, order)
+    ob = O.BlockAllocator(nb, BS32, mb, order)
+    ks, vs = workloads.pool_shapes(nb, Hkv, D, cache, BS32)
+    k = _rand_storage(gen, ks, cache, ksc)
+    v = _rand_storage(gen, vs, cache, vsc)
+    dk, dv = _to_device(k, cache), _to_device(v, cache)
+    S = len(lens)
+    ids = np.arange(S, dtype=np.int64)
+    for s in range(S):
+        assert bm.add_seq(s) == 0 and ob.add_seq(s) == 0
+    ctx = np.repeat(ids, lens - 1)
+    if len(ctx):
+        assert bm.append_slots(ctx)[0] == 0 and ob.append_slots(ctx)[0] == 0
+    _, before_tables, _ = bm.export(ids)
+    r1, s1 = bm.append_slots(ids)   # the decode token of every sequence
+    r2, s2 = ob.append_slots(ids)
+    assert r1 == r2 == 0 and np.array_equal(s1, s2)
+    _, tables, blens = bm.export(ids)
+    assert np.array_equal(blens, lens)
+    d_tables = torch.from_numpy(before_tables).cuda()
+    d_tables[torch.arange(S, device="cuda"), torch.from_numpy((lens - 1) // BS32).cuda()] = -5
+    kn = _rand_storage(gen, (S, Hkv, D), qd)
+    vn = _rand_storage(gen, (S, Hkv, D), qd)
+    G.log(f"[append decode tokens, 32-token blocks, dtype={cache}]")
+    pkv.pkv_append_decode_tokens(_to_device(kn, qd), _to_device(vn, qd), dk, dv,
+                                 torch.from_numpy(s1).cuda(),
+                                 torch.from_numpy(lens.astype(np.int32)).cuda(), d_tables, ksc, vsc)
+    O.reshape_and_cache(kn, vn, qd, k, v, cache, s2, BS32, ksc, vsc)
+    torch.cuda.synchronize()
+    assert np.array_equal(d_tables.cpu().numpy(), tables), "device tables differ"
+    assert np.array_equal(G.bits(G.np_storage(dk)), G.bits(k)), "K pool differs"
+    assert np.array_equal(G.bits(G.np_storage(dv)), G.bits(v)), "V pool differs"
