@@ -199,9 +199,12 @@ def main():
         cfg, part = (int(x) for x in wl.split(":"))
         tag = f"c{cfg}" + (f"p{part}" if part else "")
         base = ["--", py, "-u", "bench.py", "--config", str(cfg), "--partition", str(part)]
+        # the default workload is traced under exactly the default bench command
+        default = cfg == 2 and part == 0
         trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
-                     f"{a.out}/{tag}/trace", "-o", "t"] + base + [
-                     "--steps", "20", "--warmup", "3", "--no-cpu-baseline"]
+                     f"{a.out}/{tag}/trace", "-o", "t"] + (
+                     ["--", py, "-u", "bench.py"] if default else base + [
+                         "--steps", "20", "--warmup", "3", "--no-cpu-baseline"])
         line = bench_line(run(trace_cmd, f"{a.out}/{tag}_trace.log", 300))
         rows = stats_rows(f"{a.out}/{tag}/trace")
         got = {}
