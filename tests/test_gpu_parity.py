@@ -110,6 +110,22 @@ def test_partition_cuts_odd_and_even_tiles(cache, part):
     full_parity(c, label=f"partition cuts dtype={cache} part={part}")
 
 
+@pytest.mark.parametrize("cache", [BF16, E4M3])
+@pytest.mark.parametrize("part", [0, 64])
+def test_more_than_1024_sequences(cache, part):
+    """A batch past the in-kernel plan's 1024 sequences: a one-workgroup plan
+    kernel runs before pass 1, which then reads the plan from the workspace."""
+    rng = np.random.default_rng(41 + cache + part)
+    lens = rng.integers(1, 400, 1100)
+    lens[[5, 600, 1099]] = [2000, 3000, 1]
+    base = {BF16: 2, E4M3: 4}[cache]
+    spec = small_spec(250 + cache + part, base, len(lens), 16, 4, 128, lens, cache)
+    c = G.build(spec, partition_size=part)
+    seqs = np.unique(np.concatenate([[0, 5, 600, 1023, 1024, 1099],
+                                     rng.choice(len(lens), 40, replace=False)]))
+    full_parity(c, seqs, label=f"1100 seqs dtype={cache} part={part}")
+
+
 @pytest.mark.parametrize("cache", [F32, BF16, E4M3])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
