@@ -308,3 +308,31 @@ def test_append_decode_tokens_validation():
     assert call(n=0, k=None, v=None, kc=None, vc=None, slots=None, lens=None,
                 tables=None) == pkv.PKV_OK
     assert "append_decode_tokens" in L.pkv_last_error().decode()
+
+
+def prefill_params(**kw):
+    p = pkv.pkv_prefill_params()
+    base = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                max_blocks_per_seq=64, max_context_len=1024, num_query_tokens=10, num_blocks=100,
+                scale=0.088, k_scale=1.0, v_scale=1.0, q_dtype=1, cache_dtype=1, out_dtype=1)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_prefill_validation():
+    # fake, 16-byte aligned pointers: every call must be rejected (or be a no-op)
+    # by host validation before anything is enqueued
+    L = pkv.lib()
+    f = lambda p, *ptrs: L.pkv_prefill_attention(C.byref(p), *ptrs, None)
+    ok = (16, 16, 16, 16, 16, 16, 16, None)  # out q k v tables lens query_start lse
+    assert f(prefill_params(num_seqs=1025), *ok) == pkv.PKV_ERR_UNSUPPORTED
+    assert f(prefill_params(num_query_tokens=-1), *ok) == pkv.PKV_ERR_INVALID_ARG
+    assert f(prefill_params(head_dim=96), *ok) == pkv.PKV_ERR_UNSUPPORTED
+    assert f(prefill_params(num_q_heads=6, num_kv_heads=4), *ok) == pkv.PKV_ERR_INVALID_ARG
+    assert f(prefill_params(), None, 16, 16, 16, 16, 16, 16, None) == pkv.PKV_ERR_INVALID_ARG
+    assert f(prefill_params(), 16, 16, 16, 16, 16, 16, 18, None) == pkv.PKV_ERR_INVALID_ARG
+    assert f(prefill_params(num_query_tokens=0), None, None, None, None, None, None, None,
+             None) == pkv.PKV_OK
+    assert "prefill" in L.pkv_last_error().decode() or "decode" in L.pkv_last_error().decode()
