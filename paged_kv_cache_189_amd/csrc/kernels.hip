@@ -62,15 +62,6 @@ __device__ __forceinline__ uint8_t f32_to_e4m3_sat(float x) {
   return (uint8_t)(sign | code);
 }
 
-template <int SRC>
-__device__ __forceinline__ float load_src(const void* p, int64_t i) {
-  if constexpr (SRC == kF32) {
-    return static_cast<const float*>(p)[i];
-  } else {
-    return __uint_as_float((uint32_t) static_cast<const uint16_t*>(p)[i] << 16);
-  }
-}
-
 // ---------------------------------------------------------------- cache write
 // One workgroup per new token; threads stride over (kv head, 16-byte chunk).
 // With B = block_size: K chunk c of head h goes to block[h][c][slot % B][0..X);
@@ -83,7 +74,27 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
   constexpr int ES = ElemSize<CACHE>::value;
   constexpr int X = 16 / ES;
   constexpr int CH = D / X;
+  constexpr int SES = SRC == kF32 ? 4 : 2;       // source element bytes
+  constexpr int KR = X * SES / 16;               // 16-byte source pieces per item
+  struct Raw {
+    u32x4 q[KR];
+  };
   const int t = blockIdx.x;
+  const int items = a.num_kv_heads * CH;
+  // A thread's first item's sources are loaded before the slot is known, so
+  // the two loads overlap.
+  auto load_raw = [&](const void* base, int e, Raw& r) {
+    const int h = e / CH, c = e % CH;
+    const int64_t src0 = ((int64_t)t * a.num_kv_heads + h) * D + c * X;
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + src0 * SES);
+#pragma unroll
+    for (int i = 0; i < KR; ++i) r.q[i] = p[i];
+  };
+  Raw k0, v0;
+  if ((int)threadIdx.x < items) {
+    load_raw(a.k_new, threadIdx.x, k0);
+    load_raw(a.v_new, threadIdx.x, v0);
+  }
   const int64_t slot = a.slot_mapping[t];
   const int B = a.block_size;
   if (slot < 0 || slot >= a.num_blocks * B) return;
@@ -93,50 +104,61 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
     const int p = a.context_lens[t] - 1;
     if (p >= 0 && p / B < a.max_blocks) a.block_tables[(int64_t)t * a.max_blocks + p / B] = (int32_t)blk;
   }
-  for (int e = threadIdx.x; e < a.num_kv_heads * CH; e += blockDim.x) {
+  // element x of a source piece as bits (same dtype) or as a float
+  auto bits16 = [](const Raw& r, int x) -> uint16_t {
+    return reinterpret_cast<const uint16_t*>(&r)[x];
+  };
+  auto bits32 = [](const Raw& r, int x) -> uint32_t {
+    return reinterpret_cast<const uint32_t*>(&r)[x];
+  };
+  auto val = [&](const Raw& r, int x) -> float {
+    if constexpr (SRC == kF32) return __uint_as_float(bits32(r, x));
+    else return __uint_as_float((uint32_t)bits16(r, x) << 16);
+  };
+  for (int e = threadIdx.x; e < items; e += blockDim.x) {
+    Raw kr = k0, vr = v0;
+    if (e != (int)threadIdx.x) {
+      load_raw(a.k_new, e, kr);
+      load_raw(a.v_new, e, vr);
+    }
     const int h = e / CH, c = e % CH;
-    const int64_t src0 = ((int64_t)t * a.num_kv_heads + h) * D + c * X;
     const int64_t tile = (blk * a.num_kv_heads + h);
     const int64_t kdst = ((tile * CH + c) * B + off) * X;  // element index
     const int64_t vdst = (tile * D + c * X) * B + off;     // element index, stride B
     if constexpr (CACHE == SRC) {
       // same dtype: copy bits
+      static_assert(KR == 1, "one 16-byte piece per item");
       if constexpr (ES == 4) {
-        const uint32_t* ks = static_cast<const uint32_t*>(a.k_new) + src0;
-        const uint32_t* vs = static_cast<const uint32_t*>(a.v_new) + src0;
         uint32_t* kc = static_cast<uint32_t*>(a.k_cache);
         uint32_t* vc = static_cast<uint32_t*>(a.v_cache);
-        *reinterpret_cast<u32x4*>(kc + kdst) = *reinterpret_cast<const u32x4*>(ks);
+        *reinterpret_cast<u32x4*>(kc + kdst) = kr.q[0];
 #pragma unroll
-        for (int x = 0; x < X; ++x) vc[vdst + x * B] = vs[x];
+        for (int x = 0; x < X; ++x) vc[vdst + x * B] = bits32(vr, x);
       } else {
-        const uint16_t* ks = static_cast<const uint16_t*>(a.k_new) + src0;
-        const uint16_t* vs = static_cast<const uint16_t*>(a.v_new) + src0;
         uint16_t* kc = static_cast<uint16_t*>(a.k_cache);
         uint16_t* vc = static_cast<uint16_t*>(a.v_cache);
-        *reinterpret_cast<u32x4*>(kc + kdst) = *reinterpret_cast<const u32x4*>(ks);
+        *reinterpret_cast<u32x4*>(kc + kdst) = kr.q[0];
 #pragma unroll
-        for (int x = 0; x < X; ++x) vc[vdst + x * B] = vs[x];
+        for (int x = 0; x < X; ++x) vc[vdst + x * B] = bits16(vr, x);
       }
     } else if constexpr (CACHE == kBF16) {  // f32 -> bf16
       uint16_t* kc = static_cast<uint16_t*>(a.k_cache);
       uint16_t* vc = static_cast<uint16_t*>(a.v_cache);
       uint16_t kv[X];
 #pragma unroll
-      for (int x = 0; x < X; ++x) kv[x] = f32_to_bf16_rne(load_src<SRC>(a.k_new, src0 + x));
+      for (int x = 0; x < X; ++x) kv[x] = f32_to_bf16_rne(val(kr, x));
       *reinterpret_cast<u32x4*>(kc + kdst) = bitcast<u32x4>(kv);
 #pragma unroll
-      for (int x = 0; x < X; ++x) vc[vdst + x * B] = f32_to_bf16_rne(load_src<SRC>(a.v_new, src0 + x));
+      for (int x = 0; x < X; ++x) vc[vdst + x * B] = f32_to_bf16_rne(val(vr, x));
     } else {  // -> fp8 E4M3 of fp32(x / scale)
       uint8_t* kc = static_cast<uint8_t*>(a.k_cache);
       uint8_t* vc = static_cast<uint8_t*>(a.v_cache);
       uint8_t kv[X];
 #pragma unroll
-      for (int x = 0; x < X; ++x) kv[x] = f32_to_e4m3_sat(load_src<SRC>(a.k_new, src0 + x) / a.k_scale);
+      for (int x = 0; x < X; ++x) kv[x] = f32_to_e4m3_sat(val(kr, x) / a.k_scale);
       *reinterpret_cast<u32x4*>(kc + kdst) = bitcast<u32x4>(kv);
 #pragma unroll
-      for (int x = 0; x < X; ++x)
-        vc[vdst + x * B] = f32_to_e4m3_sat(load_src<SRC>(a.v_new, src0 + x) / a.v_scale);
+      for (int x = 0; x < X; ++x) vc[vdst + x * B] = f32_to_e4m3_sat(val(vr, x) / a.v_scale);
     }
   }
 }
@@ -1418,9 +1440,21 @@ __global__ __launch_bounds__(64 * kMergeRowsPerGroup) void decode_merge_rows_ker
                               : range_start(r + 1, total, R) > range_start(r, total, R));
   };
   const int nr = r_hi - r_lo + 1;
-  float mx = -INFINITY;
+  // The lane's piece among the first 64 ranges keeps its m, l and e from this
+  // pass (issued together), so the common case of a row with at most 64
+  // pieces reads them once.
+  float mx = -INFINITY, m0 = -INFINITY, l0 = 0.f, e0 = 0.f;
   for (int i = lane; i < nr; i += 64)
-    if (owns(r_lo + i)) mx = fmaxf(mx, a.ws_m[(int64_t)(k0 + r_lo + i) * G + hh]);
+    if (owns(r_lo + i)) {
+      const int64_t pr = (int64_t)(k0 + r_lo + i) * G + hh;
+      const float m = a.ws_m[pr];
+      if (i < 64) {
+        m0 = m;
+        l0 = a.ws_l[pr];
+        e0 = a.ws_e[pr];
+      }
+      mx = fmaxf(mx, m);
+    }
   const float M = wave_max(mx);
   float lam = 0.f, ex = 0.f;
   float acc[V];
@@ -1432,12 +1466,17 @@ __global__ __launch_bounds__(64 * kMergeRowsPerGroup) void decode_merge_rows_ker
     const int slot = k0 + r;
     float coef = 0.f;
     if (mine) {
-      const int64_t pr = (int64_t)slot * G + hh;
-      const float m = a.ws_m[pr];
+      float m = m0, l = l0, e = e0;
+      if (i0 > 0) {
+        const int64_t pr = (int64_t)slot * G + hh;
+        m = a.ws_m[pr];
+        l = a.ws_l[pr];
+        e = a.ws_e[pr];
+      }
       const float c = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      const float cl = c * a.ws_l[pr];
+      const float cl = c * l;
       lam += cl;
-      ex += c * a.ws_e[pr];
+      ex += c * e;
       coef = OUT == kF32 ? c : cl;  // bf16 rows are normalised by l
     }
     uint64_t left = __ballot(mine);
