@@ -138,6 +138,21 @@ def test_gqa_headdim_dtype_variants(cache, D, group):
     full_parity(c, label=f"gqa G={group} D={D} dtype={cache}")
 
 
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_decode_negative_and_zero_scale(cache, scale):
+    """Any finite softmax scale: a negative one flips which keys dominate,
+    zero gives uniform weights over the context (with partition cuts, so the
+    merge sees the same scale's states)."""
+    lens = [1, 17, 300, 2049]
+    base = {F32: 1, BF16: 2, E4M3: 4}[cache]
+    spec = small_spec(270 + cache, base, len(lens), 16, 4, 128, lens, cache)
+    c = G.build(spec, partition_size=64)
+    c.w.scale = scale
+    c.params.scale = scale
+    full_parity(c, label=f"decode scale {scale} dtype={cache}")
+
+
 def test_empty_sequence_row():
     spec = small_spec(400, 2, 3, 8, 2, 128, [33, 5, 600])
     c = G.build(spec, partition_size=64)
