@@ -1215,9 +1215,9 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // its segments are merged: M = max m_p, Lambda = sum l_p 2^{m_p - M},
 // out = sum 2^{m_p - M} o_p / Lambda, lse = (M + log2 sum e_p 2^{m_p - M}) ln 2
 // (l_p sums the weights as multiplied into V, e_p the fp32 weights).
-// The segments are listed in LDS with their factors 2^{m_p - M}; the waves
-// then take every fourth entry, each lane D/64 output dimensions, and the
-// four partial sums are added in LDS.
+// The segments are listed in LDS with their factors 2^{m_p - M}; each wave
+// then takes every fourth entry, four rows per load (lane = D/16 dims), and
+// the four waves' sums are added in LDS.
 // Lane `lane`'s V = D / 64 dims of partial row pr (fp32 or bf16 workspace).
 template <int OUT, int D>
 __device__ __forceinline__ void load_partial(const DecodeArgs& a, int64_t pr, int lane,
@@ -1240,6 +1240,40 @@ __device__ __forceinline__ void load_partial(const DecodeArgs& a, int64_t pr, in
       x[1] = __uint_as_float(t & 0xFFFF0000u);
     } else {
       x[0] = __uint_as_float((uint32_t)w[at] << 16);
+    }
+  }
+}
+
+// Dims l16 * D/16 .. + D/16 of partial row (slot, hh): 16 bytes of a bf16 row
+// (32 of an fp32 one) for D = 128, half that for D = 64.
+template <int OUT, int D>
+__device__ __forceinline__ void load_row16(const DecodeArgs& a, int64_t slot, int hh, int G,
+                                           int l16, float (&x)[D / 16]) {
+  constexpr int DPL = D / 16;
+  const int64_t at = (slot * G + hh) * D + l16 * DPL;
+  if constexpr (OUT == kF32) {
+#pragma unroll
+    for (int k = 0; k < DPL / 4; ++k) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(a.ws_o + at + 4 * k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * k + i] = t[i];
+    }
+  } else {
+    const uint16_t* w = reinterpret_cast<const uint16_t*>(a.ws_o) + at;
+    if constexpr (DPL == 8) {
+      const u32x4 t = *reinterpret_cast<const u32x4*>(w);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(t[i] << 16);
+        x[2 * i + 1] = __uint_as_float(t[i] & 0xFFFF0000u);
+      }
+    } else {
+      const u32x2 t = *reinterpret_cast<const u32x2*>(w);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        x[2 * i] = __uint_as_float(t[i] << 16);
+        x[2 * i + 1] = __uint_as_float(t[i] & 0xFFFF0000u);
+      }
     }
   }
 }
@@ -1316,28 +1350,40 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
         ++off;
       });
     __syncthreads();
-    // Four entries in flight per wave.
-    int j = wv;
-    for (; j + 3 * kMergeWaves < n; j += 4 * kMergeWaves) {
-      float x[4][V], c[4];
+    // Four rows per load instruction: lane group q = lane / 16 takes every
+    // fourth of the wave's listed entries, each lane D/16 dims of the row;
+    // four loads in flight per lane.  The groups' sums are then added across
+    // lanes.
+    constexpr int DPL = D / 16;
+    const int q = lane >> 4, l16 = lane & 15;
+    float a8[DPL];
+#pragma unroll
+    for (int v = 0; v < DPL; ++v) a8[v] = 0.f;
+    for (int e0 = wv + q * kMergeWaves; e0 < n; e0 += 16 * kMergeWaves) {
+      float x[4][DPL], c[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int e = j + u * kMergeWaves;
-        c[u] = lcoef[e];
-        load_partial<OUT, D>(a, (int64_t)lslot[e] * G + hh, lane, x[u]);
+        const int e = e0 + 4 * u * kMergeWaves;
+        c[u] = 0.f;
+        if (e < n) {
+          c[u] = lcoef[e];
+          load_row16<OUT, D>(a, lslot[e], hh, G, l16, x[u]);
+        }
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
+        if (c[u] != 0.f)
 #pragma unroll
-        for (int v = 0; v < V; ++v) acc[v] += c[u] != 0.f ? c[u] * x[u][v] : 0.f;
+          for (int v = 0; v < DPL; ++v) a8[v] += c[u] * x[u][v];
     }
-    for (; j < n; j += kMergeWaves) {
-      const float cj = lcoef[j];
-      float x[V];
-      load_partial<OUT, D>(a, (int64_t)lslot[j] * G + hh, lane, x);
 #pragma unroll
-      for (int v = 0; v < V; ++v) acc[v] += cj != 0.f ? cj * x[v] : 0.f;
+    for (int v = 0; v < DPL; ++v) {
+      a8[v] += __shfl_xor(a8[v], 16);
+      a8[v] += __shfl_xor(a8[v], 32);
     }
+    if (q == 0)
+#pragma unroll
+      for (int v = 0; v < DPL; ++v) psum[wv][l16 * DPL + v] = a8[v];
   } else {
     // Too many segments to list: each wave walks its share of the items.
     for (int i = tid; i < ps.items; i += kMergeThreads)
@@ -1359,11 +1405,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 #pragma unroll
         for (int v = 0; v < V; ++v) acc[v] += c * x[v];
       });
+#pragma unroll
+    for (int v = 0; v < V; ++v) psum[wv][lane * V + v] = acc[v];
   }
   const float Lam = block_sum(lam, red);
   const float Ex = block_sum(ex, red);
-#pragma unroll
-  for (int v = 0; v < V; ++v) psum[wv][lane * V + v] = acc[v];
   __syncthreads();
   if (tid < D) {
     float t = 0.f;
