@@ -38,9 +38,9 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention: KV GB/s and % of HBM peak; seq-tokens/s per layer"
 HBM_PEAK_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "pass1_hbm_counters.json")
-# the sources the decode kernels are built from (prefill lives apart)
+# the sources the pass-1 kernel is built from (the merge and prefill live apart)
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_189_amd", "csrc", n)
-               for n in ("kernels.hip", "device_common.h", "pkv_launch.h")]
+               for n in ("kernels.hip", "decode_plan.h", "device_common.h", "pkv_launch.h")]
 
 
 def decode_sources_sha256():

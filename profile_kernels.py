@@ -190,8 +190,8 @@ def main():
         "copy_calibration": {"bytes": copy_bytes, "fetch_kib": cal["FETCH_SIZE"],
                              "write_kib": cal["WRITE_SIZE"], "fetch_scale": scale["FETCH_SIZE"],
                              "write_scale": scale["WRITE_SIZE"]},
-        "decode_sources_hash": "sha256 of kernels.hip, device_common.h and pkv_launch.h "
-                               "concatenated, comments and white space removed",
+        "decode_sources_hash": "sha256 of kernels.hip, decode_plan.h, device_common.h and "
+                               "pkv_launch.h concatenated, comments and white space removed",
     })
     doc.setdefault("workloads", {})
 
@@ -277,8 +277,8 @@ def main():
             f"read; WRITE_SIZE {write_kib:.0f} KiB -> {wr / 1e6:.2f} MB written",
             f"- HBM bytes per launch {hbm / 1e9:.4f} GB against {alg / 1e9:.4f} GB algorithmic "
             f"({hbm / alg:.3f}x)",
-            f"- decode sources hash at measurement (sha256 of kernels.hip, device_common.h, "
-            f"pkv_launch.h with comments and white space removed): `{sha}`",
+            f"- pass-1 sources hash at measurement (sha256 of kernels.hip, decode_plan.h, "
+            f"device_common.h, pkv_launch.h with comments and white space removed): `{sha}`",
             "",
             *metric_lines(mvals, 8),
             "```",
