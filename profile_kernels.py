@@ -12,9 +12,9 @@ decode sources still hash to the value recorded there.
 
 Usage (on a machine with the GPU, from the repository root):
     python profile_kernels.py [--decode 2:0,3:0,4:0,5:512] [--prefill 2:512,4:512]
-                              [--out gpurun_out/prof]
+                              [--out DIR]
 and, where only the --out folder comes back from that machine, again with
---from-output to write the summaries from it.  rocprofv3 is started as a child
+--from-output (and the same --out) to write the summaries from it.  rocprofv3 is started as a child
 process with the Python interpreter right after `--`.
 """
 from __future__ import annotations
@@ -147,7 +147,8 @@ def main():
                     help="decode workloads, config:partition_tokens")
     ap.add_argument("--prefill", default="2:512,4:512",
                     help="prefill workloads, config:chunk_tokens ('' for none)")
-    ap.add_argument("--out", default="gpurun_out/prof")
+    ap.add_argument("--out", default="prof_out",
+                    help="folder for the rocprofv3 output and logs")
     ap.add_argument("--from-output", action="store_true",
                     help="run nothing: write the summaries from the rocprofv3 output and logs "
                          "already under --out (made by an earlier run on the GPU machine)")
