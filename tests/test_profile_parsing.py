@@ -1,0 +1,75 @@
+"""CPU tests of profile_kernels.py's parsing of rocprofv3 CSV output and bench
+lines (no GPU, no profiler): the counter figures bench.py reports as
+`roofline.traffic` come through these functions."""
+import csv
+import json
+import os
+
+import pytest
+
+import profile_kernels as P
+
+COUNTER_COLS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id",
+                "Thread_Id", "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size",
+                "LDS_Block_Size", "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count",
+                "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+
+def write_counters(d, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "t_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=COUNTER_COLS)
+        w.writeheader()
+        for disp, name, counter, value in rows:
+            r = {c: "0" for c in COUNTER_COLS}
+            r.update(Dispatch_Id=str(disp), Kernel_Name=name, Counter_Name=counter,
+                     Counter_Value=str(value))
+            w.writerow(r)
+
+
+def test_per_dispatch_sums_instances_and_filters_kernel(tmp_path):
+    d = str(tmp_path / "fetch")
+    k = "void pkv::decode_partitions_kernel<1, 128, 4, 3, true, 0>(pkv::DecodeArgs)"
+    write_counters(d, [(1, k, "FETCH_SIZE", 100.0), (1, k, "FETCH_SIZE", 50.0),   # two instances
+                       (2, k, "FETCH_SIZE", 160.0), (3, "copyBuffer", "FETCH_SIZE", 7.0),
+                       (2, k, "WRITE_SIZE", 9.0)])
+    assert sorted(P.per_dispatch(d, "FETCH_SIZE", "decode_partitions")) == [150.0, 160.0]
+    assert P.per_dispatch(d, "FETCH_SIZE", "copyBuffer") == [7.0]
+    assert P.metric_means(d, ("FETCH_SIZE",), "decode_partitions") == {"FETCH_SIZE": 155.0}
+    with pytest.raises(SystemExit):
+        P.per_dispatch(d, "FETCH_SIZE", "prefill_kernel")
+
+
+def test_unexpected_columns_are_refused(tmp_path):
+    d = tmp_path / "bad"
+    d.mkdir()
+    (d / "t_counter_collection.csv").write_text("Kernel,Value\nx,1\n")
+    with pytest.raises(SystemExit):
+        P.per_dispatch(str(d), "FETCH_SIZE", "x")
+
+
+def test_stats_rows_sorted_by_total_time(tmp_path):
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "t_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs",
+                    "MaxNs", "StdDev"])
+        w.writerow(["small", 10, 1000, 100, 1.0, 90, 110, 1])
+        w.writerow(["big", 2, 9000, 4500, 9.0, 4000, 5000, 1])
+    rows = P.stats_rows(str(d))
+    assert [r["Name"] for r in rows] == ["big", "small"]
+
+
+def test_bench_line_is_the_last_metric_json_line():
+    line = {"metric": "m", "value": 1.0}
+    text = "noise\n" + json.dumps({"metric": "old", "value": 0}) + "\n" + json.dumps(line) + "\nbye\n"
+    assert P.bench_line(text) == line
+    with pytest.raises(SystemExit):
+        P.bench_line("no json here\n")
+
+
+def test_short_names_drop_the_anonymous_namespace():
+    n = "void pkv::(anonymous namespace)::decode_merge_rows_kernel<1, 128>(pkv::DecodeArgs)"
+    assert P.short(n) == "void pkv::decode_merge_rows_kernel<1, 128>(pkv::DecodeArgs)"
+    assert P.short("x" * 200).endswith("...") and len(P.short("x" * 200)) == 91
