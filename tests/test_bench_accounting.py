@@ -8,6 +8,7 @@ totals written out by hand for small tables, including a shared prefix, a
 partially filled last block and an fp8 cache.
 """
 import dataclasses
+import os
 
 import numpy as np
 
@@ -66,3 +67,13 @@ def test_other_bytes_are_q_out_tables_and_lengths():
     S, Hq, D = 3, spec.num_q_heads, spec.head_dim
     want = S * Hq * D * (2 + 2) + 4 * (1 + 1 + 2) + 4 * S
     assert bench.other_bytes(spec, lens) == want
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=root, capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
