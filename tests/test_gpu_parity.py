@@ -94,6 +94,18 @@ def test_many_ranges_per_sequence(cache):
     full_parity(c, label=f"many ranges dtype={cache}")
 
 
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+def test_sequence_spanning_more_than_64_ranges(cache):
+    """A 100K-token sequence spans about 250 pass-1 ranges per kv head, more
+    than the merge wave has lanes: its rows take several rounds of 64 pieces;
+    the short sequences beside it finish in pass 1 or merge in one round."""
+    lens = [100_000, 1, 700, 3000, 16, 9000]
+    base = {F32: 1, BF16: 2, E4M3: 4}[cache]
+    spec = small_spec(220 + cache, base, len(lens), 32, 8, 128, lens, cache)
+    c = G.build(spec, partition_size=0)
+    full_parity(c, label=f"100K tokens dtype={cache}")
+
+
 @pytest.mark.parametrize("cache", [BF16, E4M3])
 @pytest.mark.parametrize("part", [16, 48, 96])
 def test_partition_cuts_odd_and_even_tiles(cache, part):
