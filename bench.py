@@ -77,6 +77,9 @@ def parse():
     ap.add_argument("--cold-launches", type=int, default=5,
                     help="after the timed steps, pass-1 launches each preceded by a 1 GiB read "
                          "(more than L2 + MALL), reported as roofline.cold_cache")
+    ap.add_argument("--kernel-launches", type=int, default=10,
+                    help="after the timed steps, steps with events around each kernel (append, "
+                         "pass 1, merge), reported as step_kernels")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -274,6 +277,32 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     pass1_ms = [a.elapsed_time(b) for a, b in ev]
     pass1_avg_ms = float(np.mean(pass1_ms))
+    # Each kernel of the step on its own, events around every launch, after
+    # the timed steps so their clocks stay untouched.  The append repeats the
+    # last step's (same tokens, slots and table entries: it rewrites what is
+    # there), so the state checked below is unchanged.
+    kev = []
+    for _ in range(args.kernel_launches):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        pkv.pkv_append_decode_tokens(w.k_new, w.v_new, w.k_cache, w.v_cache, d_slots, d_lens,
+                                     d_tables, w.k_scale, w.v_scale)
+        e[1].record(stream)
+        pkv.pkv_decode_attention_partitions(params, out, w.q, w.k_cache, w.v_cache, d_tables,
+                                            d_lens, ws, lse)
+        e[2].record(stream)
+        pkv.pkv_decode_attention_merge(params, out, d_lens, ws, lse)
+        e[3].record(stream)
+        kev.append(e)
+    torch.cuda.synchronize()
+    step_kernels = None
+    if kev:
+        us = np.array([[e[k].elapsed_time(e[k + 1]) * 1e3 for k in range(3)] for e in kev])
+        step_kernels = {"append_a2_us": round(float(us[:, 0].mean()), 2),
+                        "pass1_us": round(float(us[:, 1].mean()), 2),
+                        "merge_a7_us": round(float(us[:, 2].mean()), 2),
+                        "launches": len(kev),
+                        "how": "HIP events around each kernel, after the timed steps"}
 
     # Cold caches: back-to-back steps of one layer re-read the same blocks, and
     # lines kept by the default-policy loads survive in the 256 MB MALL into
@@ -345,6 +374,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": int(pass1_bytes), "avg_launch_us": round(pass1_avg_ms * 1e3, 2),
                      "timed_launches": len(ev), "cold_cache": cold},
+        "step_kernels": step_kernels,
         "setup_s": round(build_s, 1),
     }
 

@@ -135,10 +135,12 @@ def short(name, n=88):
 
 
 def stats_rows(d, top=8):
+    """The `top` kernels by total time, then every other kernel of this
+    library (the step's small kernels: cache write, merge), by total time."""
     with open(one_csv(d, "kernel_stats.csv")) as f:
         rows = list(csv.DictReader(f))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    return rows[:top]
+    return rows[:top] + [r for r in rows[top:] if "pkv::" in r["Name"]]
 
 
 def main():

@@ -61,6 +61,23 @@ def test_stats_rows_sorted_by_total_time(tmp_path):
     assert [r["Name"] for r in rows] == ["big", "small"]
 
 
+def test_stats_rows_keep_the_library_kernels_past_the_top(tmp_path):
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "t_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs",
+                    "MaxNs", "StdDev"])
+        for i in range(10):
+            w.writerow([f"other{i}", 1, 1000 * (20 - i), 1, 1.0, 1, 1, 0])
+        w.writerow(["void pkv::cache_write_kernel<1, 1>(pkv::CacheWriteArgs)", 5, 50, 10, 0.1, 9,
+                    11, 0])
+        w.writerow(["tiny", 1, 10, 10, 0.0, 10, 10, 0])
+    names = [r["Name"] for r in P.stats_rows(str(d), top=3)]
+    assert names == ["other0", "other1", "other2",
+                     "void pkv::cache_write_kernel<1, 1>(pkv::CacheWriteArgs)"]
+
+
 def test_bench_line_is_the_last_metric_json_line():
     line = {"metric": "m", "value": 1.0}
     text = "noise\n" + json.dumps({"metric": "old", "value": 0}) + "\n" + json.dumps(line) + "\nbye\n"
