@@ -179,6 +179,42 @@ def test_empty_sequence_row():
     assert np.all(np.isfinite(out[[0, 2]]))
 
 
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+@pytest.mark.parametrize("part", [0, 64])
+def test_all_sequences_empty(cache, part):
+    """No sequence has a token: pass 1 has no blocks to cut into ranges, and
+    every row is the empty row (zeros, lse = -inf)."""
+    base = {F32: 1, BF16: 2, E4M3: 4}[cache]
+    spec = small_spec(410 + cache, base, 3, 8, 2, 128, [33, 5, 600], cache)
+    c = G.build(spec, partition_size=part)
+    c.d_lens.zero_()
+    c.out.fill_(7.0)
+    G.log(f"[all empty] dtype={cache} part={part}")
+    G.run_decode(c)
+    torch.cuda.synchronize()
+    assert np.all(c.out.float().cpu().numpy() == 0)
+    assert np.all(np.isneginf(c.lse.cpu().numpy()))
+
+
+@pytest.mark.parametrize("cache", [BF16, E4M3])
+@pytest.mark.parametrize("part", [0, 64])
+def test_decode_without_lse_output(cache, part):
+    """lse_out is optional: without it the output is bit-identical."""
+    base = {BF16: 2, E4M3: 4}[cache]
+    spec = small_spec(420 + cache, base, len(RAGGED), 32, 8, 128, RAGGED, cache)
+    c = G.build(spec, partition_size=part)
+    G.log(f"[no lse] dtype={cache} part={part}")
+    G.run_cache_write(c)
+    G.run_decode(c)
+    with_lse = c.out.clone()
+    c.out.fill_(7.0)
+    w = c.w
+    pkv.pkv_decode_attention(c.params, c.out, w.q, w.k_cache, w.v_cache, c.d_tables, c.d_lens,
+                             c.workspace, None)
+    torch.cuda.synchronize()
+    assert torch.equal(c.out.view(torch.int16), with_lse.view(torch.int16))
+
+
 def test_passes_separately_equal_composed():
     spec = small_spec(401, 2, 4, 16, 4, 128, [700, 1200, 35, 2000])
     c = G.build(spec, partition_size=128)
