@@ -19,6 +19,9 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
+# A test may point the oracle at another build of oracle.c (a copy with a
+# planted mistake, to show that the pins catch it); that build is used as is.
+LIB_OVERRIDE = os.environ.get("PKV_ORACLE_LIB")
 
 F32, BF16, E4M3 = 0, 1, 2
 NP_STORAGE = {F32: np.float32, BF16: np.uint16, E4M3: np.uint8}
@@ -26,13 +29,17 @@ NP_STORAGE = {F32: np.float32, BF16: np.uint16, E4M3: np.uint8}
 OK, INVALID, OUT_OF_BLOCKS, UNKNOWN_SEQ, SEQ_EXISTS, SHARED_TAIL = 0, -1, -2, -3, -4, -5
 
 
-def build() -> str:
-    """Compile the oracle with gcc (OpenMP, no fast-math, no FMA contraction)."""
+def compile_to(src: str, out: str) -> str:
+    """Compile an oracle source with gcc (OpenMP, no fast-math, no FMA contraction)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
-           "-ffp-contract=off", SRC, "-o", LIB + ".tmp", "-lm"]
+           "-ffp-contract=off", src, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def build() -> str:
+    return compile_to(SRC, LIB)
 
 
 _lib = None
@@ -41,9 +48,12 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-            build()
-        L = C.CDLL(LIB)
+        if LIB_OVERRIDE:
+            L = C.CDLL(LIB_OVERRIDE)
+        else:
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+                build()
+            L = C.CDLL(LIB)
         P, I, I64, F, D = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_double
         L.oracle_e4m3_decode.restype = D
         L.oracle_e4m3_decode.argtypes = [C.c_uint8]
