@@ -51,6 +51,26 @@ def test_preemption_takes_the_latest_admitted():
     assert res["generated_tokens"] == 12
 
 
+def test_preemption_victim_exact_trace():
+    # 4 blocks of 4, prompts of 7 tokens (2 blocks each), outputs 2 and 6.
+    # Step 1: both append into their second block.  Step 2: request 0 needs
+    # a third block, none is free: request 1 (latest admitted) is preempted,
+    # request 0 takes a block and finishes.  Step 3: request 1 is re-admitted
+    # with its 8 tokens (2 blocks) and generates its 2nd..6th tokens over
+    # steps 3-7 (a third block at position 8, a fourth at 12).  Preempting
+    # request 0 instead would leave request 1 running in step 2.
+    res, tr = B.simulate(4, 4, 32, 8, B.PAGED, [7, 7], [2, 6])
+    assert list(tr) == [2, 0, 1, 1, 1, 1, 0]
+    assert res["preemptions"] == 1 and res["generated_tokens"] == 8 and res["iterations"] == 7
+
+
+def test_max_num_seqs_caps_concurrency():
+    # blocks to spare; six requests of 4 prompt tokens and 2 outputs with at
+    # most three running: three run two steps, then the next three
+    res, tr = B.simulate(64, 4, 64, 3, B.PAGED, [4] * 6, [2] * 6)
+    assert list(tr) == [3, 0, 3, 0] and res["peak_running"] == 3 and res["iterations"] == 4
+
+
 def test_prefix_cache_counts_shared_system_prompt():
     sysp = list(range(100, 124))                     # 24 tokens = 6 blocks of 4
     prompts = [sysp + [7, 8], sysp + [9], sysp + [1, 2, 3]]
