@@ -55,6 +55,13 @@ MUTANTS = [
      "int64_t b = slot / block_size, o = (slot / block_size) % block_size;"),
     ("split merge without the partition rescale",
      "Lam += lp[part] * exp(mp[part] - M);", "Lam += lp[part];"),
+    ("prefill: a query row skips its own token",
+     "    const int n = pos + 1;\n", "    const int n = pos > 0 ? pos : 1;\n"),
+    ("prefill: query position counted from the chunk start",
+     "const int pos = context_lens[s] - C + (int)(i - query_start[s]);",
+     "const int pos = (int)(i - query_start[s]);"),
+    ("prefill: k_scale dropped",
+     "X)) *\n                    p.k_scale;", "X));"),
     ("freed block returned to the head of the free list",
      "bm->fifo[(bm->head + bm->count) % bm->num_blocks] = blk;",
      "bm->head = (bm->head + bm->num_blocks - 1) % bm->num_blocks;\n"
