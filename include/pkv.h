@@ -300,6 +300,14 @@ size_t pkv_decode_workspace_bytes(const pkv_decode_params* p);
  * partition cuts; -1: invalid params). */
 int32_t pkv_decode_partition_size(const pkv_decode_params* p);
 
+/* The number R of pass-1 ranges (one per resident pass-1 wave) a call with
+ * these params divides the batch into on the calling thread's current
+ * device: 0 for an empty batch, -1 for invalid params or a failed device
+ * query (text in pkv_last_error).  It depends on the device and the kernel
+ * variant, not on context_lens; the partial-state slots of a call are below
+ * (split-KV partitions of all (sequence, kv head) pairs) + R. */
+int32_t pkv_decode_num_ranges(const pkv_decode_params* p);
+
 /* Both passes: per-partition attention, then the log-sum-exp merge.
  * out: [S][Hq][D] of out_dtype.  lse_out: NULL or [S][Hq] fp32.
  * workspace: device memory of at least pkv_decode_workspace_bytes(p). */

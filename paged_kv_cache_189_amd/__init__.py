@@ -38,7 +38,7 @@ EXPORTED = (
     "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_reshape_and_cache",
     "pkv_append_decode_tokens", "pkv_copy_blocks",
     "pkv_decode_workspace_bytes",
-    "pkv_decode_partition_size", "pkv_decode_attention", "pkv_decode_attention_partitions",
+    "pkv_decode_partition_size", "pkv_decode_num_ranges", "pkv_decode_attention", "pkv_decode_attention_partitions",
     "pkv_decode_attention_merge", "pkv_prefill_attention", "pkv_sim_run", "pkv_status_string",
     "pkv_last_error", "pkv_version",
 )
@@ -123,6 +123,7 @@ def lib():
             "pkv_copy_blocks": (st, [P, P, st, P, P, I32, I32, I32, I32, I64, P]),
             "pkv_decode_workspace_bytes": (C.c_size_t, [C.POINTER(pkv_decode_params)]),
             "pkv_decode_partition_size": (I32, [C.POINTER(pkv_decode_params)]),
+            "pkv_decode_num_ranges": (I32, [C.POINTER(pkv_decode_params)]),
             "pkv_decode_attention": (st, [C.POINTER(pkv_decode_params), P, P, P, P, P, P, P,
                                           C.c_size_t, P, P]),
             "pkv_decode_attention_partitions": (st, [C.POINTER(pkv_decode_params), P, P, P, P, P,
@@ -349,6 +350,14 @@ def pkv_decode_workspace_bytes(params: pkv_decode_params) -> int:
 
 def pkv_decode_partition_size(params: pkv_decode_params) -> int:
     return int(lib().pkv_decode_partition_size(C.byref(params)))
+
+
+def pkv_decode_num_ranges(params: pkv_decode_params) -> int:
+    """Pass-1 ranges on the current device (raises on invalid params)."""
+    r = int(lib().pkv_decode_num_ranges(C.byref(params)))
+    if r < 0:
+        raise PkvError(PKV_ERR_INVALID_ARG, "pkv_decode_num_ranges")
+    return r
 
 
 def _ws(workspace):

@@ -33,27 +33,31 @@ struct Layout {
   size_t cum_off = 0, parts_off = 0, rpair_off = 0, bytes = 0;
 };
 
-// Workspace: fp32 partial states of at most max_segments segment slots, then
-// the plan arrays.  Slots are below (partitions of all pairs) + ranges; a pair
-// has at most ceil(blocks / part_blocks) partitions (1 without partition
-// cuts), and ranges are at most kMaxRanges.
-Layout layout_of(const pkv_decode_params& p) {
+// Workspace: the partial states of at most max_segments segment slots (rows
+// of D elements: fp32 for fp32 outputs, bf16 otherwise; m, l, e in fp32),
+// then the plan arrays.  Slots are below (partitions of all pairs) + ranges;
+// a pair has at most ceil(blocks / part_blocks) partitions (1 without
+// partition cuts).  `ranges` bounds the pass-1 range count: kMaxRanges for a
+// caller's workspace, whose size must not depend on the device; the
+// device's own count where the library sizes the memory itself.
+Layout layout_of(const pkv_decode_params& p, int64_t ranges = pkv::kMaxRanges) {
   Layout L;
   L.part_blocks = p.partition_size > 0 ? p.partition_size / kTile : 0;
   const int64_t max_blocks = ((int64_t)(p.max_context_len > 0 ? p.max_context_len : 0) + kTile - 1) / kTile;
   const int64_t pieces = L.part_blocks > 0 ? (max_blocks + L.part_blocks - 1) / L.part_blocks : 1;
   const int64_t pairs = (int64_t)p.num_seqs * p.num_kv_heads;
   const int64_t group = p.num_kv_heads > 0 ? p.num_q_heads / p.num_kv_heads : 1;
-  L.max_segments = pairs * (pieces > 1 ? pieces : 1) + pkv::kMaxRanges;
+  L.max_segments = pairs * (pieces > 1 ? pieces : 1) + ranges;
   const size_t rows = (size_t)L.max_segments * (size_t)group;
+  const size_t o_elem = p.out_dtype == PKV_F32 ? 4 : 2;
   L.o_off = 0;
-  L.m_off = round_up(rows * (size_t)p.head_dim * sizeof(float), 256);
+  L.m_off = round_up(rows * (size_t)p.head_dim * o_elem, 256);
   L.l_off = L.m_off + round_up(rows * sizeof(float), 256);
   L.e_off = L.l_off + round_up(rows * sizeof(float), 256);
   L.cum_off = L.e_off + round_up(rows * sizeof(float), 256);
   L.parts_off = L.cum_off + round_up(((size_t)p.num_seqs + 1) * sizeof(int32_t), 256);
   L.rpair_off = L.parts_off + round_up(((size_t)p.num_seqs + 1) * sizeof(int32_t), 256);
-  L.bytes = L.rpair_off + round_up((size_t)pkv::kMaxRanges * sizeof(int32_t), 256);
+  L.bytes = L.rpair_off + round_up((size_t)ranges * sizeof(int32_t), 256);
   return L;
 }
 
@@ -286,6 +290,20 @@ size_t pkv_decode_workspace_bytes(const pkv_decode_params* p) {
 int32_t pkv_decode_partition_size(const pkv_decode_params* p) {
   if (check_decode(p) != PKV_OK) return -1;
   return layout_of(*p).part_blocks * kTile;
+}
+
+int32_t pkv_decode_num_ranges(const pkv_decode_params* p) {
+  if (check_decode(p) != PKV_OK) return -1;
+  if (p->num_seqs == 0) return 0;
+  hipError_t e = hipSuccess;
+  const int r = pkv::decode_ranges(p->cache_dtype, p->head_dim, p->num_seqs, p->block_size == 32 ? 1 : 0,
+                                   (int64_t)p->num_seqs * p->num_kv_heads * ((int64_t)p->max_context_len + kTile - 1) / kTile,
+                                   &e);
+  if (e != hipSuccess) {
+    check_hip(e, "decode_num_ranges: querying the device");
+    return -1;
+  }
+  return r;
 }
 
 pkv_status pkv_prefill_attention(const pkv_prefill_params* p, void* out, const void* q, const void* k_cache,

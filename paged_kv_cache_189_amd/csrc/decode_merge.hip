@@ -284,13 +284,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
     float t = 0.f;
 #pragma unroll
     for (int k = 0; k < kMergeWaves; ++k) t += psum[k][tid];
-    const float val = Lam > 0.f ? t / Lam : 0.f;
+    const float val = !(Lam <= 0.f) ? t / Lam : 0.f;
     if constexpr (OUT == kF32)
       static_cast<float*>(a.out)[(int64_t)row * D + tid] = val;
     else
       static_cast<uint16_t*>(a.out)[(int64_t)row * D + tid] = f32_to_bf16_rne(val);
   }
-  if (tid == 0 && a.lse) a.lse[row] = Ex > 0.f ? (M + __builtin_amdgcn_logf(Ex)) * kLn2 : -INFINITY;
+  if (tid == 0 && a.lse) a.lse[row] = !(Ex <= 0.f) ? (M + __builtin_amdgcn_logf(Ex)) * kLn2 : -INFINITY;
 }
 
 // Without partition cuts, the segments of a (sequence, kv head) pair are
@@ -422,14 +422,14 @@ __global__ __launch_bounds__(64 * kMergeRowsPerGroup) void decode_merge_rows_ker
   if constexpr (OUT == kF32) {
 #pragma unroll
     for (int v = 0; v < V; ++v)
-      static_cast<float*>(a.out)[(int64_t)row * D + lane * V + v] = Lam > 0.f ? acc[v] / Lam : 0.f;
+      static_cast<float*>(a.out)[(int64_t)row * D + lane * V + v] = !(Lam <= 0.f) ? acc[v] / Lam : 0.f;
   } else {
 #pragma unroll
     for (int v = 0; v < V; ++v)
       static_cast<uint16_t*>(a.out)[(int64_t)row * D + lane * V + v] =
-          f32_to_bf16_rne(Lam > 0.f ? acc[v] / Lam : 0.f);
+          f32_to_bf16_rne(!(Lam <= 0.f) ? acc[v] / Lam : 0.f);
   }
-  if (lane == 0 && a.lse) a.lse[row] = Ex > 0.f ? (M + __builtin_amdgcn_logf(Ex)) * kLn2 : -INFINITY;
+  if (lane == 0 && a.lse) a.lse[row] = !(Ex <= 0.f) ? (M + __builtin_amdgcn_logf(Ex)) * kLn2 : -INFINITY;
 }
 
 }  // namespace

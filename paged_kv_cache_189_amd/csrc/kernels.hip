@@ -745,11 +745,19 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
     run_tiles(std::integral_constant<bool, SH == 0>{}, b_end);
   }
   if (absorb >= 0) {
-    // The publisher finishes its piece before or, when that piece is its
-    // whole range, about when this wave does; the bound only guards against
-    // a hang.
+    // The publisher is the next wave of this workgroup, co-resident with
+    // this one; it publishes right after its first piece, and a wait only
+    // ever points to a higher wave (the last never waits), so the chain is at
+    // most NW - 1 long and ends.  The bound (2^24 sleeps, about half a
+    // second) only guards against a hang; if it ever ran out, the piece would
+    // be lost, so the state becomes NaN and the row (or partial state) this
+    // wave writes says so instead of holding a silently wrong value.
+    bool got = false;
     for (int spin = 0; spin < (1 << 24); ++spin) {
-      if (__hip_atomic_load(&flag[absorb], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) break;
+      if (__hip_atomic_load(&flag[absorb], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0) {
+        got = true;
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
     const FoldLds<KIND, D>& f = fold[absorb];
@@ -762,6 +770,13 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
     st.e = ca * st.e + cb * f.e[lane];
 #pragma unroll
     for (int nt = 0; nt < T::NT; ++nt) st.acc.o[nt] = ca * st.acc.o[nt] + cb * f.o[nt][lane];
+    if (!got) {
+      st.m = __builtin_nanf("");
+      st.l = st.m;
+      st.e = st.m;
+#pragma unroll
+      for (int nt = 0; nt < T::NT; ++nt) st.acc.o[nt] = f32x4{st.m, st.m, st.m, st.m};
+    }
   }
   if (publish >= 0) {
     FoldLds<KIND, D>& f = fold[publish];
@@ -794,7 +809,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * D + d) = u32x2{lo, hi};
       }
     }
-    if (q4 == 0 && a.lse) a.lse[row] = e_run > 0.f ? (m_run + __builtin_amdgcn_logf(e_run)) * kLn2 : -INFINITY;
+    if (q4 == 0 && a.lse) a.lse[row] = !(e_run <= 0.f) ? (m_run + __builtin_amdgcn_logf(e_run)) * kLn2 : -INFINITY;
   } else {
     const int64_t pr = (int64_t)slot * G + r;
     store_partial<KIND, D>(a, slot, G, r, q4, st.acc.o, l_run);

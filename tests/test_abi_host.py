@@ -213,15 +213,17 @@ def params(**kw):
 MAX_RANGES = 16384
 
 
-def _ws_expected(S, Hq, Hkv, D, max_ctx, part_tokens):
-    """Partial states for (partitions of all pairs + ranges) slots, then the
-    prefix sums of blocks and partitions per sequence and each range's first pair."""
+def _ws_expected(S, Hq, Hkv, D, max_ctx, part_tokens, out_bytes=2):
+    """Partial states for (partitions of all pairs + ranges) slots -- rows of
+    D output-dtype elements (fp32 for fp32 outputs, bf16 otherwise) and fp32
+    m, l, e -- then the prefix sums of blocks and partitions per sequence and
+    each range's first pair."""
     r256 = lambda x: -(-x // 256) * 256
     blocks = -(-max_ctx // 16)
     pieces = -(-blocks // (part_tokens // 16)) if part_tokens else 1
     segs = S * Hkv * max(pieces, 1) + MAX_RANGES
     rows = segs * (Hq // Hkv)
-    return (r256(rows * D * 4) + 3 * r256(rows * 4) + 2 * r256((S + 1) * 4)
+    return (r256(rows * D * out_bytes) + 3 * r256(rows * 4) + 2 * r256((S + 1) * 4)
             + r256(MAX_RANGES * 4))
 
 
@@ -231,7 +233,10 @@ def test_workspace_and_partition_sizing():
     assert pkv.pkv_decode_workspace_bytes(p) == _ws_expected(2, 8, 2, 128, 1024, 0)
     assert pkv.pkv_decode_partition_size(params(partition_size=256)) == 256
     assert pkv.pkv_decode_workspace_bytes(params(partition_size=256)) == _ws_expected(2, 8, 2, 128, 1024, 256)
+    f32 = dict(q_dtype=0, cache_dtype=0, out_dtype=0)
+    assert pkv.pkv_decode_workspace_bytes(params(**f32)) == _ws_expected(2, 8, 2, 128, 1024, 0, 4)
     assert pkv.pkv_decode_workspace_bytes(params(head_dim=96)) == 0  # invalid -> 0
+    assert pkv.lib().pkv_decode_num_ranges(C.byref(params(head_dim=96))) == -1
 
 
 @pytest.mark.parametrize("bad,status", [

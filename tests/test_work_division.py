@@ -54,6 +54,7 @@ def pass1(nblocks, H, R, pb):
     total = T * H
     partial, final = {}, {}
     covered = {}
+    events = []  # (range, pair, 'publish' | 'absorb')
     fold_on = pb == 0 and total >= R
     for rg in range(R):
         w = rg % NW
@@ -77,6 +78,11 @@ def pass1(nblocks, H, R, pb):
             cov = covered.setdefault((g, s), np.zeros(nblk, dtype=np.int64))
             cov[lo:hi] += 1
             publish = fold_on and x == x_first and lo > 0 and w != 0
+            absorb = fold_on and ps + hi == x1 and hi < nblk and w != NW - 1
+            if publish:
+                events.append((rg, (g, s), "publish"))
+            if absorb:
+                events.append((rg, (g, s), "absorb"))
             if fold_on:
                 whole = lo == 0 and range_of(pe - 1, total, R) // NW == rg // NW
             else:
@@ -91,7 +97,7 @@ def pass1(nblocks, H, R, pb):
                     assert slot + k not in partial, "slot written twice"
                     partial[slot + k] = (g, s)
             x = ps + hi
-    return partial, final, covered, PT
+    return partial, final, covered, PT, events
 
 
 def merge_reads(nblocks, H, R, pb):
@@ -143,7 +149,8 @@ def merge_reads(nblocks, H, R, pb):
 
 def check(nblocks, H, R, pb):
     nblocks = [int(n) for n in nblocks]
-    partial, final, covered, PT = pass1(nblocks, H, R, pb)
+    partial, final, covered, PT, events = pass1(nblocks, H, R, pb)
+    check_fold_waits(events, R)
     reads, skipped = merge_reads(nblocks, H, R, pb)
     S = len(nblocks)
     # every tile of every pair covered exactly once
@@ -166,6 +173,36 @@ def check(nblocks, H, R, pb):
     assert set(final) == skipped & nonempty_pairs
     assert all(v == 1 for v in final.values())
     assert not set(final) & set(partial.values())
+
+
+def check_fold_waits(events, R):
+    """The LDS fold's waits, as pass 1 takes them: wave w of a workgroup that
+    absorbs waits for a publish by wave w + 1 of the same workgroup, for the
+    same pair.  Checked: every absorb has exactly that publish and every
+    publish is absorbed (no piece is dropped); the last wave never waits, so
+    a wave waits only on higher waves of its workgroup, each wave waits at
+    most once and publishes at most once, and the longest chain of waits
+    (w -> w + 1 -> ...) is at most NW - 1 long: no cycle, every wait ends."""
+    pub = {}
+    absorbs = {}
+    for rg, pair, kind in events:
+        table = pub if kind == "publish" else absorbs
+        assert rg not in table, f"range {rg} {kind}es twice"
+        table[rg] = pair
+    for rg, pair in absorbs.items():
+        assert rg % NW != NW - 1, "the last wave of a workgroup waits"
+        assert pub.get(rg + 1) == pair, f"range {rg} waits for a publish that never comes"
+    for rg, pair in pub.items():
+        assert rg % NW != 0, "the first wave of a workgroup publishes"
+        assert absorbs.get(rg - 1) == pair, f"range {rg} publishes a piece nobody absorbs"
+    # chains of waits: w waits on w + 1 (which may itself wait on w + 2)
+    for rg in absorbs:
+        n, r = 0, rg
+        while r in absorbs:
+            n += 1
+            r += 1
+            assert r // NW == rg // NW, "a wait leaves its workgroup"
+        assert n <= NW - 1
 
 
 @pytest.mark.parametrize("seed", range(6))
@@ -194,4 +231,9 @@ def test_benchmark_workloads(index, pb):
     (two waves per SIMD on 256 CUs: 2048); partition 512 tokens = 32 tiles."""
     spec = workloads.SPECS[index]
     lens = workloads.lengths(spec)
-    check([(int(L) + 15) // 16 for L in lens], spec.num_kv_heads, 2048, pb)
+    nblocks = [(int(L) + 15) // 16 for L in lens]
+    check(nblocks, spec.num_kv_heads, 2048, pb)
+    if pb == 0:  # the fold is on, and its waits reach the longest chain (3)
+        events = pass1(nblocks, spec.num_kv_heads, 2048, pb)[4]
+        absorbs = {rg for rg, _, kind in events if kind == "absorb"}
+        assert any(rg in absorbs and rg + 1 in absorbs and rg + 2 in absorbs for rg in absorbs)
