@@ -31,7 +31,9 @@
  *    the text of the calling thread's last failure.
  *  - Host pointers are read or written only during the call.
  *  - Device pointers are caller-owned device memory.  The library never
- *    allocates or frees device memory.  Device operations are enqueued on
+ *    allocates or frees device memory; its one device array of its own is
+ *    the fixed scratch of pkv_decode_attention_noalloc (below), which the
+ *    HIP loader places once per GPU.  Device operations are enqueued on
  *    `stream` (a hipStream_t; NULL = the null stream), never synchronise,
  *    and their buffers must outlive the enqueued work.
  *  - Arguments are validated on the host before anything is enqueued; a
@@ -339,6 +341,31 @@ pkv_status pkv_decode_attention_partitions(const pkv_decode_params* p, void* out
 pkv_status pkv_decode_attention_merge(const pkv_decode_params* p, void* out,
                                       const int32_t* context_lens, const void* workspace,
                                       size_t workspace_bytes, float* lse_out, void* stream);
+
+/* Decode attention that allocates nothing, for callers that cannot call
+ * hipMalloc or take a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, kernels and
+ * results (bit for bit) as pkv_decode_attention, without the workspace: the
+ * partial states and the plan live in a static device array of the library,
+ * PKV_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it runs on, held until the
+ * process ends.  The call uses the copy of the calling thread's current
+ * device (`stream` must belong to it); the array's address on that device is
+ * looked up on the first call there.  Calls whose partial states and plan
+ * need more (the bound of pkv_decode_workspace_bytes, with the device's own
+ * range count, pkv_decode_num_ranges, in place of the 16384 it assumes)
+ * return PKV_ERR_UNSUPPORTED with the size in pkv_last_error and enqueue
+ * nothing -- e.g. 8 sequences of 128 query heads over 131072 tokens with
+ * 512-token partitions need ~76 MB, the same without partition cuts ~9 MB.
+ * Nothing in the array needs to start at zero.  Every call on a GPU shares
+ * that GPU's array and leaves its contents there: two calls that overlap on
+ * one GPU (other streams, other threads) race and give wrong results, so
+ * order them on one stream. */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+pkv_status pkv_decode_attention_noalloc(const pkv_decode_params* p, void* out, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables,
+                                        const int32_t* context_lens, float* lse_out,
+                                        void* stream);
 
 /* ======================================================================== */
 /* Chunked prefill attention over the paged cache                            */

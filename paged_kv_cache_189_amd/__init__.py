@@ -38,7 +38,8 @@ EXPORTED = (
     "pkv_bm_num_free_blocks", "pkv_bm_refcount", "pkv_reshape_and_cache",
     "pkv_append_decode_tokens", "pkv_copy_blocks",
     "pkv_decode_workspace_bytes",
-    "pkv_decode_partition_size", "pkv_decode_num_ranges", "pkv_decode_attention", "pkv_decode_attention_partitions",
+    "pkv_decode_partition_size", "pkv_decode_num_ranges", "pkv_decode_attention",
+    "pkv_decode_attention_noalloc", "pkv_decode_attention_partitions",
     "pkv_decode_attention_merge", "pkv_prefill_attention", "pkv_sim_run", "pkv_status_string",
     "pkv_last_error", "pkv_version",
 )
@@ -126,6 +127,8 @@ def lib():
             "pkv_decode_num_ranges": (I32, [C.POINTER(pkv_decode_params)]),
             "pkv_decode_attention": (st, [C.POINTER(pkv_decode_params), P, P, P, P, P, P, P,
                                           C.c_size_t, P, P]),
+            "pkv_decode_attention_noalloc": (st, [C.POINTER(pkv_decode_params), P, P, P, P, P,
+                                                  P, P, P]),
             "pkv_decode_attention_partitions": (st, [C.POINTER(pkv_decode_params), P, P, P, P, P,
                                                      P, P, C.c_size_t, P, P]),
             "pkv_decode_attention_merge": (st, [C.POINTER(pkv_decode_params), P, P, P, C.c_size_t,
@@ -374,6 +377,21 @@ def pkv_decode_attention(params: pkv_decode_params, out: torch.Tensor, q: torch.
     _check(lib().pkv_decode_attention(
         C.byref(params), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
         _ptr(context_lens), wp, wb, _ptr(lse), _stream(stream, out)), "pkv_decode_attention")
+
+
+PKV_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pkv_decode_attention_noalloc(params: pkv_decode_params, out: torch.Tensor, q: torch.Tensor,
+                                 k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                 lse: Optional[torch.Tensor] = None, stream=None):
+    """pkv_decode_attention without a workspace: the library's own scratch of
+    the current device holds the partial states (calls on one device must be
+    ordered on one stream)."""
+    _check(lib().pkv_decode_attention_noalloc(
+        C.byref(params), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(lse), _stream(stream, out)), "pkv_decode_attention_noalloc")
 
 
 def pkv_decode_attention_partitions(params, out, q, k_cache, v_cache, block_tables,

@@ -1,10 +1,11 @@
 // C ABI of libpkv: argument validation, kernel dispatch, workspace sizing and
 // error reporting for the device operations declared in include/pkv.h.
 // Every check runs on the host before anything is enqueued.
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "../../include/pkv.h"
@@ -99,13 +100,48 @@ pkv_status check_hip(hipError_t e, const char* what) {
   return pkv_fail(PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// ---------------------------------------------------------------- scratch
+// Device memory of the allocation-free decode call: a file-scope device
+// array, one copy per GPU, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is a stand-in, not a
+// device address): the address comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and kept per device.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device; null until the first call there
+
+// The scratch array's address on the current device (looked up on the
+// first call there).
+pkv_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return check_hip(e, "decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode_noalloc: device index >= 64");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return check_hip(e, "decode_noalloc: hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return pkv_fail(PKV_ERR_HIP, "decode_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+// Validates the call and fills the kernel arguments.  The partial states and
+// the plan live in the caller's workspace, or (own_scratch) in the library's
+// scratch array of the current device, laid out for that device's range
+// count.
 pkv_status build_args(const pkv_decode_params* p, void* out, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                       const void* workspace, size_t workspace_bytes, float* lse_out, bool need_q_cache,
-                      pkv::DecodeArgs* a, Layout* lay) {
+                      bool own_scratch, pkv::DecodeArgs* a) {
   pkv_status st = check_decode(p);
   if (st != PKV_OK) return st;
-  const Layout L = layout_of(*p);
+  Layout L = layout_of(*p);
   if (p->num_seqs > 0) {
     if (!out || !context_lens) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: out and context_lens are required");
     if (need_q_cache && (!q || !k_cache || !v_cache || !block_tables))
@@ -115,11 +151,35 @@ pkv_status build_args(const pkv_decode_params* p, void* out, const void* q, cons
                           !aligned(block_tables, 4))) ||
         (lse_out && !aligned(lse_out, 4)))
       return pkv_fail(PKV_ERR_INVALID_ARG, "decode: q and the caches must be 16-byte aligned, other arrays element aligned");
-    if (!workspace || workspace_bytes < L.bytes)
-      return pkv_fail(PKV_ERR_INVALID_ARG, "decode: workspace missing or smaller than pkv_decode_workspace_bytes()");
-    if (!aligned(workspace, 256)) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: workspace must be 256-byte aligned");
+    if (!own_scratch) {
+      if (!workspace || workspace_bytes < L.bytes)
+        return pkv_fail(PKV_ERR_INVALID_ARG, "decode: workspace missing or smaller than pkv_decode_workspace_bytes()");
+      if (!aligned(workspace, 256)) return pkv_fail(PKV_ERR_INVALID_ARG, "decode: workspace must be 256-byte aligned");
+    }
   }
   pkv::DecodeArgs& d = *a;
+  d.num_ranges = 0;
+  d.block_shift = p->block_size == 32 ? 1 : 0;
+  // ranges of pass 1 (one per resident wave); pass 2 derives the same slots
+  if (p->num_seqs > 0) {
+    hipError_t e = hipSuccess;
+    d.num_ranges = pkv::decode_ranges(p->cache_dtype, p->head_dim, p->num_seqs, d.block_shift,
+                                      (int64_t)p->num_seqs * p->num_kv_heads * ((int64_t)p->max_context_len + kTile - 1) / kTile,
+                                      &e);
+    if (e != hipSuccess) return check_hip(e, "decode: querying the device");
+  }
+  if (own_scratch && p->num_seqs > 0) {
+    L = layout_of(*p, d.num_ranges);
+    if (L.bytes > (size_t)PKV_NOALLOC_SCRATCH_BYTES)
+      return pkv_fail(PKV_ERR_UNSUPPORTED,
+                      "decode_noalloc: these params need " + std::to_string(L.bytes) +
+                          " bytes of partial states and plan; the library's scratch holds " +
+                          std::to_string((size_t)PKV_NOALLOC_SCRATCH_BYTES) + " per device");
+    void* ptr = nullptr;
+    st = scratch_of_current_device(&ptr);
+    if (st != PKV_OK) return st;
+    workspace = ptr;
+  }
   d.out = out;
   d.q = q;
   d.k_cache = k_cache;
@@ -143,19 +203,8 @@ pkv_status build_args(const pkv_decode_params* p, void* out, const void* q, cons
   d.max_blocks = p->max_blocks_per_seq;
   d.max_context_len = p->max_context_len;
   d.part_blocks = L.part_blocks;
-  d.block_shift = p->block_size == 32 ? 1 : 0;
-  d.num_ranges = 0;
   d.score_scale_log2 = (float)((double)p->scale * (double)p->k_scale * 1.4426950408889634);
   d.v_scale = p->v_scale;
-  *lay = L;
-  // ranges of pass 1 (one per resident wave); pass 2 derives the same slots
-  if (p->num_seqs > 0) {
-    hipError_t e = hipSuccess;
-    d.num_ranges = pkv::decode_ranges(p->cache_dtype, p->head_dim, p->num_seqs, d.block_shift,
-                                      (int64_t)p->num_seqs * p->num_kv_heads * ((int64_t)p->max_context_len + kTile - 1) / kTile,
-                                      &e);
-    if (e != hipSuccess) return check_hip(e, "decode: querying the device");
-  }
   return PKV_OK;
 }
 
@@ -372,9 +421,8 @@ pkv_status pkv_decode_attention_partitions(const pkv_decode_params* p, void* out
                                            const int32_t* context_lens, void* workspace, size_t workspace_bytes,
                                            float* lse_out, void* stream) {
   pkv::DecodeArgs a;
-  Layout L;
   pkv_status st = build_args(p, out, q, k_cache, v_cache, block_tables, context_lens, workspace, workspace_bytes,
-                             lse_out, true, &a, &L);
+                             lse_out, true, false, &a);
   if (st != PKV_OK) return st;
   bool ok = false;
   hipError_t e = pkv::launch_decode_partitions(a, p->cache_dtype, p->head_dim, (hipStream_t)stream, &ok);
@@ -385,9 +433,8 @@ pkv_status pkv_decode_attention_partitions(const pkv_decode_params* p, void* out
 pkv_status pkv_decode_attention_merge(const pkv_decode_params* p, void* out, const int32_t* context_lens,
                                       const void* workspace, size_t workspace_bytes, float* lse_out, void* stream) {
   pkv::DecodeArgs a;
-  Layout L;
   pkv_status st = build_args(p, out, nullptr, nullptr, nullptr, nullptr, context_lens, workspace, workspace_bytes,
-                             lse_out, false, &a, &L);
+                             lse_out, false, false, &a);
   if (st != PKV_OK) return st;
   bool ok = false;
   hipError_t e = pkv::launch_decode_merge(a, p->out_dtype, p->head_dim, (hipStream_t)stream, &ok);
@@ -399,9 +446,8 @@ pkv_status pkv_decode_attention(const pkv_decode_params* p, void* out, const voi
                                 const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                                 void* workspace, size_t workspace_bytes, float* lse_out, void* stream) {
   pkv::DecodeArgs a;
-  Layout L;
   pkv_status st = build_args(p, out, q, k_cache, v_cache, block_tables, context_lens, workspace, workspace_bytes,
-                             lse_out, true, &a, &L);
+                             lse_out, true, false, &a);
   if (st != PKV_OK) return st;
   bool ok = false;
   hipError_t e = pkv::launch_decode_partitions(a, p->cache_dtype, p->head_dim, (hipStream_t)stream, &ok);
@@ -411,6 +457,24 @@ pkv_status pkv_decode_attention(const pkv_decode_params* p, void* out, const voi
   e = pkv::launch_decode_merge(a, p->out_dtype, p->head_dim, (hipStream_t)stream, &ok);
   if (!ok) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode: no merge kernel variant");
   return check_hip(e, "decode merge launch");
+}
+
+pkv_status pkv_decode_attention_noalloc(const pkv_decode_params* p, void* out, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, const int32_t* context_lens,
+                                        float* lse_out, void* stream) {
+  pkv::DecodeArgs a;
+  pkv_status st = build_args(p, out, q, k_cache, v_cache, block_tables, context_lens, nullptr, 0, lse_out,
+                             true, true, &a);
+  if (st != PKV_OK) return st;
+  bool ok = false;
+  hipError_t e = pkv::launch_decode_partitions(a, p->cache_dtype, p->head_dim, (hipStream_t)stream, &ok);
+  if (!ok) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode_noalloc: no kernel variant");
+  st = check_hip(e, "decode_noalloc partitions launch");
+  if (st != PKV_OK) return st;
+  e = pkv::launch_decode_merge(a, p->out_dtype, p->head_dim, (hipStream_t)stream, &ok);
+  if (!ok) return pkv_fail(PKV_ERR_UNSUPPORTED, "decode_noalloc: no merge kernel variant");
+  return check_hip(e, "decode_noalloc merge launch");
 }
 
 }  // extern "C"
