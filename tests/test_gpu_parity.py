@@ -338,22 +338,32 @@ def test_cache_write_bit_exact(src, dst, D):
 
 
 # ------------------------------------------------------------------- full sizes, sampled
-def sample_seqs(lens, k, seed):
-    order = np.argsort(lens)
-    pick = {int(order[0]), int(order[-1])}
-    rng = np.random.default_rng(seed)
-    while len(pick) < min(k, len(lens)):
-        pick.add(int(rng.integers(0, len(lens))))
-    return np.array(sorted(pick))
-
-
-@pytest.mark.parametrize("index,k", [(2, 64), (3, 24), (4, 8), (5, 2)])
-def test_full_size_config_sampled(index, k):
+@pytest.mark.parametrize("index,k,part", [(2, 64, None), (3, 32, None), (4, 32, None),
+                                          (4, 12, 48), (5, 8, None)])
+def test_full_size_config_sampled(index, k, part):
+    """Each workload at full size in the launch configuration the benchmark
+    times.  The sample is chosen by the CPU model of the work division
+    (tests/test_work_division.py) at this device's range count, so that it
+    holds sequences meeting each case of it: pieces folded between waves
+    (publish, absorb), pairs finished in pass 1 and merged in pass 2, more
+    than 64 pieces in one merge, range boundaries at odd tiles (the fp8
+    block-pair stages mask half a pair there), partition cuts at range
+    starts.  The 70B fp8 workload is also run with 48-token partitions, an
+    odd number of tiles, which sends its segments to the 16-token tile loop."""
+    from tests import test_work_division as WD
     spec = workloads.SPECS[index]
-    G.log(f"[config {index}] building {spec.name}")
-    c = G.build(spec)
-    seqs = sample_seqs(c.lens, k, index)
-    full_parity(c, seqs, label=f"config {index} full size, {len(seqs)} sampled seqs")
+    G.log(f"[config {index} part={part}] building {spec.name}")
+    c = G.build(spec, partition_size=part)
+    R = pkv.pkv_decode_num_ranges(c.params)
+    pb = pkv.pkv_decode_partition_size(c.params) // BS
+    nblocks = [-(-int(L) // BS) for L in c.lens]
+    flags = WD.case_flags(nblocks, spec.num_kv_heads, R, pb)
+    cases = WD.FULL_SIZE_CASES.get((index, pb), ())
+    seqs = WD.targeted_sample(flags, c.lens, k, cases, index)
+    for case in cases:
+        assert any(case in flags[int(s)] for s in seqs), f"no sampled sequence meets {case} (R={R})"
+    G.log(f"[config {index} part={part}] R={R}, {len(seqs)} seqs covering {sorted(cases)}")
+    full_parity(c, seqs, label=f"config {index} part={part} full size, {len(seqs)} sampled seqs")
     del c
 
 

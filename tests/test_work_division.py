@@ -55,6 +55,7 @@ def pass1(nblocks, H, R, pb):
     partial, final = {}, {}
     covered = {}
     events = []  # (range, pair, 'publish' | 'absorb')
+    segs = []  # (range, pair, lo, hi): the tiles [lo, hi) of the pair this range takes
     fold_on = pb == 0 and total >= R
     for rg in range(R):
         w = rg % NW
@@ -75,6 +76,7 @@ def pass1(nblocks, H, R, pb):
             lo = x - ps
             hi = min(nblk, x1 - ps)
             pe = ps + nblk
+            segs.append((rg, (g, s), lo, hi))
             cov = covered.setdefault((g, s), np.zeros(nblk, dtype=np.int64))
             cov[lo:hi] += 1
             publish = fold_on and x == x_first and lo > 0 and w != 0
@@ -97,7 +99,7 @@ def pass1(nblocks, H, R, pb):
                     assert slot + k not in partial, "slot written twice"
                     partial[slot + k] = (g, s)
             x = ps + hi
-    return partial, final, covered, PT, events
+    return partial, final, covered, PT, events, segs
 
 
 def merge_reads(nblocks, H, R, pb):
@@ -149,7 +151,7 @@ def merge_reads(nblocks, H, R, pb):
 
 def check(nblocks, H, R, pb):
     nblocks = [int(n) for n in nblocks]
-    partial, final, covered, PT, events = pass1(nblocks, H, R, pb)
+    partial, final, covered, PT, events, _ = pass1(nblocks, H, R, pb)
     check_fold_waits(events, R)
     reads, skipped = merge_reads(nblocks, H, R, pb)
     S = len(nblocks)
@@ -173,6 +175,67 @@ def check(nblocks, H, R, pb):
     assert set(final) == skipped & nonempty_pairs
     assert all(v == 1 for v in final.values())
     assert not set(final) & set(partial.values())
+
+
+def case_flags(nblocks, H, R, pb):
+    """Which work-division cases each sequence meets (under some kv head):
+      publish / absorb   its piece in a range is handed to, or takes in, the
+                         piece of the neighbouring wave of a workgroup (fold);
+      whole              a pair finished inside pass 1 (final row there);
+      merged             a pair left to pass 2;
+      merge_gt64         pass 2 merges more than 64 pieces of a pair;
+      odd_cut            a range boundary falls inside the pair at an odd
+                         16-token tile (the fp8 block-pair stages then mask
+                         one half of a pair);
+      cut_at_range_start a partition cut coincides with a range start;
+      range_in_partition a range start falls strictly inside a partition.
+    Returns {sequence: set of case names}."""
+    nblocks = [int(n) for n in nblocks]
+    S = len(nblocks)
+    partial, final, _, PT, events, segs = pass1(nblocks, H, R, pb)
+    reads, _ = merge_reads(nblocks, H, R, pb)
+    cb, _ = plan(nblocks, pb)
+    total = cb[S] * H
+    starts = {range_start(r, total, R) for r in range(R)}
+    flags = {s: set() for s in range(S)}
+    for rg, (g, s), kind in events:
+        flags[s].add(kind)
+    for (g, s) in final:
+        flags[s].add("whole")
+    for (g, s), slots in reads.items():
+        flags[s].add("merged")
+        if len(slots) > 64:
+            flags[s].add("merge_gt64")
+    for rg, (g, s), lo, hi in segs:
+        if lo > 0 and lo % 2 == 1:
+            flags[s].add("odd_cut")
+    if pb > 0:
+        for g in range(H):
+            for s in range(S):
+                ps = g * cb[-1] + cb[s]
+                for i in range((nblocks[s] + pb - 1) // pb):
+                    a, b = ps + i * pb, min(ps + (i + 1) * pb, ps + nblocks[s])
+                    if i > 0 and a in starts:
+                        flags[s].add("cut_at_range_start")
+                    if any(a < x < b for x in (range_start(range_of(b - 1, total, R), total, R),)):
+                        flags[s].add("range_in_partition")
+    return flags
+
+
+def targeted_sample(flags, lens, k, cases, seed):
+    """Up to two sequences per case, the shortest and the longest, then
+    random ones up to k (all when k >= the batch)."""
+    S = len(lens)
+    if k >= S:
+        return np.arange(S)
+    pick = {int(np.argmin(lens)), int(np.argmax(lens))}
+    for c in cases:
+        hit = [s for s in range(S) if c in flags[s]]
+        pick.update(hit[:2])
+    rng = np.random.default_rng(seed)
+    while len(pick) < k:
+        pick.add(int(rng.integers(0, S)))
+    return np.array(sorted(pick))
 
 
 def check_fold_waits(events, R):
@@ -237,3 +300,25 @@ def test_benchmark_workloads(index, pb):
         events = pass1(nblocks, spec.num_kv_heads, 2048, pb)[4]
         absorbs = {rg for rg, _, kind in events if kind == "absorb"}
         assert any(rg in absorbs and rg + 1 in absorbs and rg + 2 in absorbs for rg in absorbs)
+
+
+# the cases the full-size GPU parity samples must contain, per workload and
+# partition (in 16-token tiles)
+FULL_SIZE_CASES = {
+    (3, 0): ("publish", "absorb", "whole", "merged"),
+    (4, 0): ("publish", "absorb", "whole", "merged", "odd_cut"),
+    (4, 3): ("merged", "cut_at_range_start", "range_in_partition", "odd_cut"),
+    (5, 32): ("merged", "merge_gt64", "cut_at_range_start", "range_in_partition"),
+}
+
+
+@pytest.mark.parametrize("index,pb", list(FULL_SIZE_CASES))
+def test_full_size_workloads_meet_every_case(index, pb):
+    """At the range count of bf16 and fp8 D=128 on MI355X (2048), the
+    workloads' own length draws meet every case their GPU parity sample must
+    contain."""
+    spec = workloads.SPECS[index]
+    lens = workloads.lengths(spec)
+    flags = case_flags([(int(L) + 15) // 16 for L in lens], spec.num_kv_heads, 2048, pb)
+    for c in FULL_SIZE_CASES[(index, pb)]:
+        assert any(c in f for f in flags.values()), c
