@@ -12,11 +12,29 @@ sequences, i.e. the whole hot path:
 Inputs are resident in HBM before the timed region; each step decodes the
 next token, so contexts grow by one per step.
 
-Prints one JSON line.  `value` is KV GB/s over the whole step (algorithmic
-KV bytes / step time); `roofline` is the pass-1 kernel's algorithmic bytes
-per launch over its HIP-event-timed average duration, against 8 TB/s.  The
-events bracket pass 1 on every fifth timed step (at least ten launches): an
-event pair costs ~6 us of step time, which the other steps do not pay.
+Default workload: the 70B-shaped layer with an fp8 E4M3 KV cache (256
+sequences, the largest of the five), with the other full-size workloads
+(Llama-3-8B-shaped, 70B with a shared prefix, 405B long context with 512-token
+partitions) measured the same way and reported in the same line.
+
+Timing protocol per workload: W untimed warm-up steps; then K timed steps,
+each preceded by a 1 GiB read that evicts L2 and the 256 MB MALL (a model's
+other layers would have evicted them between two steps of one layer), each
+bracketed by HIP events on the launch stream (step: from the metadata copy
+to the end of the merge; pass 1 alone; pass 1 + pass 2); then K warm steps
+back to back, timed by the wall clock; then a few steps with events around
+every kernel.  `value`, `ms_per_step` and `roofline` are the flushed figures;
+the warm ones sit beside them.  The timed region (the K flushed steps,
+flushes included) is bracketed by synchronizations; its wall time is reported
+too.
+
+After the timed steps the state of each workload's last step is checked
+against the fp64 oracle on a sample of sequences: the oracle gets the
+generated pool as it was before any library write, its own allocator's
+tables, and its own cache write of every token the steps appended.  On the
+default workload the same oracle run, repeated, is the CPU baseline.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -24,9 +42,9 @@ import argparse
 import dataclasses
 import hashlib
 import json
-import re
 import math
 import os
+import re
 import sys
 import time
 
@@ -41,6 +59,8 @@ COUNTERS = os.path.join(ROOT, "profiles", "pass1_hbm_counters.json")
 # the sources the pass-1 kernel is built from (the merge and prefill live apart)
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_189_amd", "csrc", n)
                for n in ("kernels.hip", "decode_plan.h", "device_common.h", "pkv_launch.h")]
+FLUSH_BYTES = 1 << 30
+TOL = {0: None, 1: 1e-2, 2: 3e-2}  # by cache dtype: fp32 is 1e-5 of each row's largest |value|
 
 
 def decode_sources_sha256():
@@ -59,11 +79,13 @@ def decode_sources_sha256():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload index (1-5)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, help="headline workload (1-5)")
+    ap.add_argument("--others", default="2,3,5",
+                    help="further workloads measured and reported in the same line ('none' for none)")
     ap.add_argument("--partition", type=int, default=-1,
-                    help="tokens per split-KV partition (-1: the workload's choice)")
+                    help="tokens per split-KV partition of the headline workload (-1: its own)")
     ap.add_argument("--block-size", type=int, default=16, choices=(16, 32),
                     help="tokens per physical KV block")
     ap.add_argument("--op", default="decode", choices=("decode", "prefill", "sim"),
@@ -72,14 +94,14 @@ def parse():
     ap.add_argument("--chunk", type=int, default=512,
                     help="query tokens per sequence for --op prefill (the last ones of each context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=0,
-                    help="sequences in the oracle sample (0: the default for the workload)")
-    ap.add_argument("--cold-launches", type=int, default=5,
-                    help="after the timed steps, pass-1 launches each preceded by a 1 GiB read "
-                         "(more than L2 + MALL), reported as roofline.cold_cache")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle check of the final state")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU work of the repeated oracle run behind cpu_baseline")
     ap.add_argument("--kernel-launches", type=int, default=10,
                     help="after the timed steps, steps with events around each kernel (append, "
                          "pass 1, merge), reported as step_kernels")
+    ap.add_argument("--no-probe", action="store_true", help="skip the read-bandwidth probe")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -88,7 +110,9 @@ def parse():
 # Split-KV partition size per workload (tokens); 0 = balanced ranges only.
 # The 405B-shaped long-context workload is specified with 512-token partitions.
 PARTITION = {1: 0, 2: 0, 3: 0, 4: 0, 5: 512}
-CPU_SEQS = {1: 4, 2: 64, 3: 32, 4: 8, 5: 1}
+# sequences of each workload checked against the oracle (and, for the
+# headline, timed as the CPU baseline)
+PARITY_SEQS = {1: 4, 2: 8, 3: 8, 4: 8, 5: 1}
 
 
 def kv_bytes(spec, tables, lens):
@@ -151,44 +175,187 @@ def traffic_from_counters(key):
         return None
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
-              "not sharded across GPUs in this library.", file=sys.stderr)
-        sys.exit(2)
-    import torch
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
-    import paged_kv_cache_189_amd as pkv
-    import workloads
 
-    if args.copy_probe_mib:
-        copy_probe(args.copy_probe_mib)
-        return
-    if args.op == "sim":
-        sim_bench(args)
-        return
-    if args.op == "prefill":
-        prefill_bench(args)
-        return
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    pkv.lib()
+def job_cores():
+    cores = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():  # the share this job was given
+        cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
+    return cores
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ read ceiling
+def read_ceiling(pkv, torch, gib=4):
+    """The read-bandwidth probe over `gib` GiB (more than L2 + MALL): a
+    contiguous sweep (default policy, non-temporal) and 4 KiB tiles in a
+    shuffled order (non-temporal), three timed launches each; GB/s of each
+    and the best."""
     dev = torch.device("cuda:0")
-    spec = dataclasses.replace(workloads.SPECS[args.config], block_size=args.block_size)
+    nbytes = gib << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    buf.random_(0, 1 << 30)
+    grid = 256 * 32
+    sink = torch.zeros(grid * 256, dtype=torch.int32, device=dev)
+    tile = 4096
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    order = torch.randperm(nbytes // tile, device=dev, generator=gen).to(torch.int32)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, mode in (("sweep_default", 0), ("sweep_nontemporal", 1), ("tiles_4k_shuffled_nt", 2)):
+        kw = dict(order=order, tile_bytes=tile) if mode == 2 else {}
+        pkv.pkv_read_probe(buf, mode, sink, grid=grid, **kw)  # warm-up
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pkv.pkv_read_probe(buf, mode, sink, grid=grid, **kw)
+            e1.record(stream)
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = min(a.elapsed_time(b) for a, b in ts)
+        res[name] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf, order, sink
+    torch.cuda.empty_cache()
+    res["best_gbs"] = max(res.values())
+    res["bytes"] = nbytes
+    res["how"] = "pkv_read_probe, best of 3 event-timed launches per form"
+    return res
+
+
+# ------------------------------------------------------------------ one workload
+class OracleSample:
+    """The oracle's view of a sample of sequences at the final step, made
+    before the library writes anything: the generated pool bytes of the
+    blocks the sequences will hold, gathered from the device, with tables
+    from the oracle's own allocator replaying the run's appends."""
+
+    def __init__(self, spec, w, order, num_blocks, max_blocks, lens0, n_steps, k, torch):
+        from oracle import oracle as O
+        import workloads
+        BS = spec.block_size
+        S = len(lens0)
+        ob = O.BlockAllocator(num_blocks, BS, max_blocks, order)
+        workloads.allocate_context(ob, spec, lens0)
+        ids = np.arange(S, dtype=np.int64)
+        for _ in range(n_steps - 1):
+            rc, _ = ob.append_slots(ids)
+            assert rc == 0, rc
+        _, tables, lens = ob.export(ids)
+        # sequences: evenly spread over the batch, the longest included
+        seqs = np.unique(np.concatenate([np.linspace(0, S - 1, min(k, S)).round().astype(np.int64),
+                                         [int(np.argmax(lens))]]))
+        n = [-(-int(lens[s]) // BS) for s in seqs]
+        blocks = np.unique(np.concatenate([tables[s, :n[i]] for i, s in enumerate(seqs)]))
+        remap = np.full(int(tables.max()) + 1, -1, dtype=np.int64)
+        remap[blocks] = np.arange(len(blocks))
+        t = np.full((len(seqs), tables.shape[1]), -1, dtype=np.int32)
+        for i, s in enumerate(seqs):
+            t[i, :n[i]] = remap[tables[s, :n[i]]]
+        idx = torch.from_numpy(blocks.astype(np.int64)).to(w.k_cache.device)
+        self.kc = self.host(w.k_cache.index_select(0, idx), torch)
+        self.vc = self.host(w.v_cache.index_select(0, idx), torch)
+        sel = torch.from_numpy(seqs).to(w.q.device)
+        self.q = np.ascontiguousarray(self.host(w.q.index_select(0, sel), torch))
+        kn = self.host(w.k_new.index_select(0, sel), torch)
+        vn = self.host(w.v_new.index_select(0, sel), torch)
+        # every token the run appends: positions lens0 - 1 .. lens - 1, each
+        # with its sequence's new K and V
+        rows, slots = [], []
+        for i, s in enumerate(seqs):
+            for p in range(int(lens0[s]) - 1, int(lens[s])):
+                rows.append(i)
+                slots.append(int(t[i, p // BS]) * BS + p % BS)
+        rows = np.array(rows)
+        self.kn_all = np.ascontiguousarray(kn[rows])
+        self.vn_all = np.ascontiguousarray(vn[rows])
+        self.slots_all = np.array(slots, dtype=np.int64)
+        # the last step's tokens alone (the timed CPU step)
+        last = np.cumsum([int(lens[s]) - int(lens0[s]) + 1 for s in seqs]) - 1
+        self.kn_last = np.ascontiguousarray(kn)
+        self.vn_last = np.ascontiguousarray(vn)
+        self.slots_last = self.slots_all[last]
+        self.seqs, self.tables, self.lens = seqs, t, lens[seqs].astype(np.int32)
+        self.lens_all = lens
+        self.spec, self.w = spec, w
+
+    @staticmethod
+    def host(x, torch):
+        x = x.cpu()
+        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
+
+    def write_all(self):
+        from oracle import oracle as O
+        s, w = self.spec, self.w
+        O.reshape_and_cache(self.kn_all, self.vn_all, s.q_dtype, self.kc, self.vc, s.cache_dtype,
+                            self.slots_all, s.block_size, w.k_scale, w.v_scale)
+
+    def step(self, threads, seqs=None):
+        """The oracle's decode step on the sample: cache write of the last
+        step's tokens (rewriting what write_all put there) and fp64
+        attention.  seqs: indices into the sample (default all)."""
+        from oracle import oracle as O
+        s, w = self.spec, self.w
+        i = np.arange(len(self.seqs)) if seqs is None else np.asarray(seqs)
+        O.reshape_and_cache(self.kn_last[i], self.vn_last[i], s.q_dtype, self.kc, self.vc,
+                            s.cache_dtype, self.slots_last[i], s.block_size, w.k_scale, w.v_scale)
+        return O.decode_attention(self.q[i], s.q_dtype, self.kc, self.vc, s.cache_dtype,
+                                  self.tables[i], self.lens[i], s.num_kv_heads, s.block_size,
+                                  w.scale, w.k_scale, w.v_scale, threads=threads)
+
+
+def compare(spec, got, got_lse, ref, ref_lse):
+    """Max error of the GPU rows against the oracle's, and whether it meets
+    the bar of the cache dtype."""
+    got = got.astype(np.float64)
+    err = np.abs(got - ref)
+    tol = TOL[spec.cache_dtype]
+    if tol is None:
+        rowmax = np.maximum(np.abs(ref).max(axis=2, keepdims=True), 1e-300)
+        metric = float((err / rowmax).max())
+        ok = metric <= 1e-5
+        kind = "max |err| / row max |ref|"
+    else:
+        metric = float(err.max())
+        ok = metric <= tol
+        kind = "max abs err"
+    fin = np.isfinite(ref_lse)
+    lerr = float(np.abs(got_lse[fin] - ref_lse[fin]).max() / max(1.0, np.abs(ref_lse[fin]).max())) \
+        if fin.any() else 0.0
+    ok = ok and bool(np.all(np.isfinite(got))) and np.array_equal(fin, np.isfinite(got_lse)) \
+        and lerr <= 1e-4
+    return {"max_err": metric, "kind": kind, "tol": tol if tol is not None else 1e-5,
+            "lse_rel_err": lerr, "ok": bool(ok)}
+
+
+def run_workload(args, index, part_arg, pkv, torch, flush, sink, headline):
+    import workloads
+    dev = torch.device("cuda:0")
+    spec = dataclasses.replace(workloads.SPECS[index], block_size=args.block_size)
     BS = spec.block_size
-    part = PARTITION[args.config] if args.partition < 0 else args.partition
-    total_steps = args.warmup + args.steps
+    part = PARTITION[index] if part_arg < 0 else part_arg
+    W, K = args.warmup, args.steps
+    n_steps = W + 2 * K  # warm-up, flushed, warm; the first uses the context's own decode token
     lens0 = workloads.lengths(spec)
     S = len(lens0)
     t_build = time.perf_counter()
     w = workloads.make(spec, device=dev, lens=lens0)
-    # table wide enough for the tokens this run appends
-    width = w.max_blocks * BS + total_steps + BS
+    width = w.max_blocks * BS + n_steps + BS
     max_blocks = -(-width // BS)
-    nb_extra = S * (-(-total_steps // BS) + 1)
-    # grow the pool for the appended tokens (fresh blocks hold N(0,1)-free garbage;
-    # they are written by the cache write before they are read)
-    if nb_extra:
+    nb_extra = S * (-(-n_steps // BS) + 1)
+    if nb_extra:  # room for the appended tokens (written before they are read)
         ks, vs = workloads.pool_shapes(nb_extra, spec.num_kv_heads, spec.head_dim, spec.cache_dtype,
                                        BS)
         w.k_cache = torch.cat([w.k_cache, torch.zeros(ks, dtype=w.k_cache.dtype, device=dev)])
@@ -200,12 +367,12 @@ def main():
     ids = np.arange(S, dtype=np.int64)
     _, tables0, blens = bm.export(ids)
     workloads.poison_unused(w, tables0[:, : w.max_blocks], lens0 - 1)
+    sample = None
+    if not args.no_parity or (headline and not args.no_cpu_baseline):
+        sample = OracleSample(spec, w, order, num_blocks, max_blocks, lens0, n_steps,
+                              PARITY_SEQS[index], torch)
 
     out_dtype = torch.float32 if spec.out_dtype == workloads.F32 else torch.bfloat16
-    # Device block tables are copied once; afterwards a step sends its slots
-    # and lengths in one small packed buffer, and the decode append that
-    # writes the new tokens' K/V also sets each sequence's table entry for
-    # its new position (a fresh block at a block boundary).
     d_tables = torch.from_numpy(tables0).to(dev)
     meta_bytes = 8 * S + 4 * S
 
@@ -219,7 +386,6 @@ def main():
     ws = torch.empty(max(pkv.pkv_decode_workspace_bytes(params), 256), dtype=torch.uint8, device=dev)
     out = torch.empty(w.q.shape, dtype=out_dtype, device=dev)
     lse = torch.empty((S, spec.num_q_heads), dtype=torch.float32, device=dev)
-    # two pinned host buffers for the per-step metadata
     pin = []
     for _ in range(2):
         hb = torch.empty(meta_bytes, dtype=torch.uint8, pin_memory=True)
@@ -231,14 +397,12 @@ def main():
     torch.cuda.synchronize()
     build_s = time.perf_counter() - t_build
 
-    lens_per_step = []  # every timed step
-    ev, ev_lens = [], []  # the event-timed pass-1 launches and their lengths
+    def do_flush():
+        sink.add_(flush.sum())  # a 1 GiB read: evicts L2 and the MALL, leaves no dirty lines
 
-    # pass 1 is bracketed by events on every EVENT_EVERY-th timed step
-    event_every = max(1, min(5, args.steps // 10))
-
-    def step(i, timed):
-        sampled = timed and (i - args.warmup) % event_every == 0
+    def step(i, ev=None):
+        """One decode step; ev = (e0, p0, p1, e1) events: step start, pass 1
+        start and end, step end."""
         buf = pin[i % 2]
         copied[i % 2].synchronize()  # the copy that last read this buffer is done
         sl, ln = buf["slots"].numpy(), buf["lens"].numpy()
@@ -249,38 +413,49 @@ def main():
             assert rc == 0, rc
             host_lens[:] += 1
             ln[:] = host_lens
+        lens_now = ln.copy()
+        if ev is not None:
+            do_flush()
+            ev[0].record(stream)
         d_meta.copy_(buf["raw"], non_blocking=True)
         copied[i % 2].record(stream)
         pkv.pkv_append_decode_tokens(w.k_new, w.v_new, w.k_cache, w.v_cache, d_slots,  # a2
                                      d_lens, d_tables, w.k_scale, w.v_scale)
-        if sampled:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+        if ev is not None:
+            ev[1].record(stream)
         pkv.pkv_decode_attention_partitions(params, out, w.q, w.k_cache, w.v_cache, d_tables,
                                             d_lens, ws, lse)                     # a3-a6, a8
-        if sampled:
-            e1.record(stream)
-            ev.append((e0, e1))
-            ev_lens.append(ln.copy())
-        if timed:
-            lens_per_step.append(ln.copy())
+        if ev is not None:
+            ev[2].record(stream)
         pkv.pkv_decode_attention_merge(params, out, d_lens, ws, lse)             # a7
+        if ev is not None:
+            ev[3].record(stream)
+        return lens_now
 
-    for i in range(args.warmup):
-        step(i, False)
+    for i in range(W):
+        step(i)
     torch.cuda.synchronize()
+    # flushed, event-timed steps (the headline protocol)
+    evs, lens_flushed = [], []
     t0 = time.perf_counter()
-    for i in range(args.warmup, total_steps):
-        step(i, True)
+    for i in range(W, W + K):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        lens_flushed.append(step(i, e))
+        evs.append(e)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    pass1_ms = [a.elapsed_time(b) for a, b in ev]
-    pass1_avg_ms = float(np.mean(pass1_ms))
-    # Each kernel of the step on its own, events around every launch, after
-    # the timed steps so their clocks stay untouched.  The append repeats the
-    # last step's (same tokens, slots and table entries: it rewrites what is
-    # there), so the state checked below is unchanged.
+    flushed_wall_s = time.perf_counter() - t0
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    pass1_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    attn_ms = np.array([e[1].elapsed_time(e[3]) for e in evs])
+    # warm steps back to back, wall clock
+    lens_warm = []
+    t0 = time.perf_counter()
+    for i in range(W + K, n_steps):
+        lens_warm.append(step(i))
+    torch.cuda.synchronize()
+    warm_step_ms = (time.perf_counter() - t0) * 1e3 / K
+    # each kernel on its own, warm (the append repeats the last step's tokens
+    # and slots, which rewrites what is there)
     kev = []
     for _ in range(args.kernel_launches):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -295,92 +470,220 @@ def main():
         e[3].record(stream)
         kev.append(e)
     torch.cuda.synchronize()
-    step_kernels = None
-    if kev:
-        us = np.array([[e[k].elapsed_time(e[k + 1]) * 1e3 for k in range(3)] for e in kev])
-        step_kernels = {"append_a2_us": round(float(us[:, 0].mean()), 2),
-                        "pass1_us": round(float(us[:, 1].mean()), 2),
-                        "merge_a7_us": round(float(us[:, 2].mean()), 2),
-                        "launches": len(kev),
-                        "how": "HIP events around each kernel, after the timed steps"}
+    us = np.array([[e[k].elapsed_time(e[k + 1]) * 1e3 for k in range(3)] for e in kev]) \
+        if kev else np.full((1, 3), np.nan)
 
-    # Cold caches: back-to-back steps of one layer re-read the same blocks, and
-    # lines kept by the default-policy loads survive in the 256 MB MALL into
-    # the next step, which a model's other layers would evict.  These launches
-    # repeat pass 1 on the final state, each after reading 1 GiB (which evicts
-    # L2 and MALL without leaving dirty lines to drain during pass 1).
-    cold = None
-    if args.cold_launches > 0:
-        flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
-        sink = torch.zeros((), dtype=torch.float32, device=dev)
-        sink.add_(flush.sum())  # the zero fill's dirty lines drain here
-        cev = []
-        for _ in range(args.cold_launches):
-            sink.add_(flush.sum())
-            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c0.record(stream)
-            pkv.pkv_decode_attention_partitions(params, out, w.q, w.k_cache, w.v_cache, d_tables,
-                                                d_lens, ws, lse)
-            c1.record(stream)
-            pkv.pkv_decode_attention_merge(params, out, d_lens, ws, lse)
-            cev.append((c0, c1))
-        torch.cuda.synchronize()
-        cold_ms = float(np.mean([a.elapsed_time(b) for a, b in cev]))
-        del flush
-
-    # algorithmic bytes, step by step (contexts grow by one token per step)
-    _, tables_now, lens_now = bm.export(ids)
     # the device tables kept by the decode append must equal the manager's
+    _, tables_now, lens_now = bm.export(ids)
     assert np.array_equal(d_tables.cpu().numpy(), tables_now), "device block tables drifted"
     assert np.array_equal(lens_now, host_lens), "context lengths drifted"
-    kv_u, kv_l = [], []
-    for ln in lens_per_step:
-        u, l = kv_bytes(spec, tables_now, ln)
-        kv_u.append(u)
-        kv_l.append(l)
-    kv_step = float(np.mean(kv_u))
-    pass1_bytes = float(np.mean([kv_bytes(spec, tables_now, ln)[0] + other_bytes(spec, ln)
-                                 for ln in ev_lens]))
-    achieved = pass1_bytes / (pass1_avg_ms * 1e-3) / 1e9
-    value = kv_step / (ms_per_step * 1e-3) / 1e9
-    seq_tok_s = S / (ms_per_step * 1e-3)
 
-    if cold is None and args.cold_launches > 0:
-        cold_bytes = kv_bytes(spec, tables_now, host_lens)[0] + other_bytes(spec, host_lens)
-        cold_gbs = cold_bytes / (cold_ms * 1e-3) / 1e9
-        cold = {"achieved": round(cold_gbs, 1), "frac": round(cold_gbs / HBM_PEAK_GBS, 4),
-                "avg_launch_us": round(cold_ms * 1e3, 2), "launches": args.cold_launches,
-                "before_each": "1 GiB read (evicts L2 and MALL)"}
+    def kv(ln):
+        return kv_bytes(spec, tables_now, ln)
 
-    counters = traffic_from_counters(workload_key(args.config, part, BS))
-    traffic = counters.get("hbm_bytes_per_launch") if counters else None
-
+    kv_f = np.array([kv(ln)[0] for ln in lens_flushed], dtype=np.float64)
+    kv_fl = np.array([kv(ln)[1] for ln in lens_flushed], dtype=np.float64)
+    p1_f = kv_f + np.array([other_bytes(spec, ln) for ln in lens_flushed], dtype=np.float64)
+    kv_w = np.array([kv(ln)[0] for ln in lens_warm], dtype=np.float64)
+    p1_last = kv(host_lens)[0] + other_bytes(spec, host_lens)
+    flushed_gbs = float(np.mean(kv_f / (step_ms * 1e-3)) / 1e9)
+    p1_gbs = float(np.mean(p1_f / (pass1_ms * 1e-3)) / 1e9)
+    warm_p1_gbs = float(p1_last / (np.mean(us[:, 1]) * 1e-6) / 1e9)
     res = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {workloads.F32: "f32", workloads.BF16: "bf16",
-                  workloads.E4M3: "fp8-e4m3 kv, bf16 q/out"}[spec.cache_dtype],
-        "data": "synthetic (seeded N(0,1) values, shuffled block tables)",
-        "config": {"workload": spec.name, "seqs": S, "q_heads": spec.num_q_heads,
-                   "kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim, "block_size": BS,
-                   "partition_tokens": pkv.pkv_decode_partition_size(params),
-                   "mean_context": float(np.mean(lens_per_step[0])), "parallelism": "1 GPU"},
-        "seq_tokens_per_s_per_layer": round(seq_tok_s, 1),
-        "kv_bytes_per_step": int(kv_step),
-        "kv_bytes_per_step_logical": int(np.mean(kv_l)),
-        "roofline": {"bound": "hbm", "kernel": "decode_partitions_kernel (pass 1)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": int(pass1_bytes), "avg_launch_us": round(pass1_avg_ms * 1e3, 2),
-                     "timed_launches": len(ev), "cold_cache": cold},
-        "step_kernels": step_kernels,
+        "workload": spec.name, "index": index, "seqs": S,
+        "partition_tokens": pkv.pkv_decode_partition_size(params), "block_size": BS,
+        "pass1_ranges": pkv.pkv_decode_num_ranges(params),
+        "mean_context": float(np.mean(lens_flushed[0])),
+        "kv_bytes_per_step": int(np.mean(kv_f)), "kv_bytes_per_step_logical": int(np.mean(kv_fl)),
+        "pass1_bytes_per_launch": int(np.mean(p1_f)),
+        "flushed": {
+            "step_ms": round(float(np.mean(step_ms)), 4),
+            "step_ms_median": round(float(np.median(step_ms)), 4),
+            "step_ms_min": round(float(np.min(step_ms)), 4),
+            "kv_gbs": round(flushed_gbs, 1),
+            "seq_tokens_per_s_per_layer": round(S / (np.mean(step_ms) * 1e-3), 1),
+            "attention_us": round(float(np.mean(attn_ms)) * 1e3, 2),
+            "attention_us_median": round(float(np.median(attn_ms)) * 1e3, 2),
+            "attention_us_min": round(float(np.min(attn_ms)) * 1e3, 2),
+            "pass1_us": round(float(np.mean(pass1_ms)) * 1e3, 2),
+            "pass1_gbs": round(p1_gbs, 1), "pass1_frac": round(p1_gbs / HBM_PEAK_GBS, 4),
+            "steps": K, "wall_s_incl_flushes": round(flushed_wall_s, 4)},
+        "warm": {
+            "step_ms": round(warm_step_ms, 4),
+            "kv_gbs": round(float(np.mean(kv_w)) / (warm_step_ms * 1e-3) / 1e9, 1),
+            "seq_tokens_per_s_per_layer": round(S / (warm_step_ms * 1e-3), 1),
+            "pass1_us": round(float(np.mean(us[:, 1])), 2),
+            "pass1_gbs": round(warm_p1_gbs, 1), "pass1_frac": round(warm_p1_gbs / HBM_PEAK_GBS, 4),
+            "steps": K},
+        "step_kernels": {"append_a2_us": round(float(us[:, 0].mean()), 2),
+                         "pass1_us": round(float(us[:, 1].mean()), 2),
+                         "merge_a7_us": round(float(us[:, 2].mean()), 2),
+                         "launches": len(kev), "how": "HIP events around each kernel, warm"},
         "setup_s": round(build_s, 1),
     }
+    counters = traffic_from_counters(workload_key(index, part, BS))
+    res["traffic"] = counters.get("hbm_bytes_per_launch") if counters else None
+    res["dtype"] = {workloads.F32: "f32", workloads.BF16: "bf16",
+                    workloads.E4M3: "fp8-e4m3 kv, bf16 q/out"}[spec.cache_dtype]
+    if sample is not None:
+        assert np.array_equal(sample.lens_all, lens_now), "oracle allocator lengths differ"
+        sample.write_all()
+        cores = job_cores()
+        t0 = time.perf_counter()
+        ref, ref_lse = sample.step(cores)
+        first_s = time.perf_counter() - t0
+        sel = torch.from_numpy(sample.seqs).to(dev)
+        got = out.index_select(0, sel).float().cpu().numpy()
+        got_lse = lse.index_select(0, sel).cpu().numpy().astype(np.float64)
+        if not args.no_parity:
+            res["parity"] = dict(compare(spec, got, got_lse, ref, ref_lse),
+                                 seqs=[int(s) for s in sample.seqs],
+                                 what="final step's output and lse vs the fp64 oracle")
+        if headline and not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline(spec, sample, cores, first_s, args.cpu_seconds)
+    del w, ws, out, lse, d_tables
+    torch.cuda.empty_cache()
+    return res
 
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(spec, w, bm, ids, args, pkv, torch)
+
+def cpu_baseline(spec, sample, cores, first_s, seconds):
+    """The fp64 oracle, untuned, on the sample: its cache write of the
+    step's tokens and its attention over the sampled sequences, repeated for
+    about `seconds`; then once on one thread over the shortest sampled
+    sequence."""
+    import workloads
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        sample.step(cores)
+        reps += 1
+        secs = time.perf_counter() - t0
+        if secs + first_s >= seconds or reps >= 50:
+            break
+    per_tok = 2 * spec.num_kv_heads * spec.head_dim * workloads.ELEM_BYTES[spec.cache_dtype]
+    k = len(sample.seqs)
+    toks = int(np.sum(sample.lens))
+    kvb = toks * per_tok * reps
+    j = int(np.argmin(sample.lens))  # the shortest sampled sequence
+    t1 = time.perf_counter()
+    sample.step(1, [j])
+    one_s = time.perf_counter() - t1
+    one_tok = int(sample.lens[j])
+    return {"value": round(kvb / secs / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "seq_tokens_per_s_per_layer": round(k * reps / secs, 2), "seconds": round(secs, 2),
+            "cpu_model": cpu_model(),
+            "sample": f"{k} of {spec.num_seqs} sequences of the final step (all "
+                      f"{spec.num_q_heads} query heads, {toks} tokens), cache write + fp64 "
+                      f"attention, repeated {reps}x on {cores} threads",
+            "one_thread": {"value": round(one_tok * per_tok / one_s / 1e9, 4), "unit": "GB/s",
+                           "seconds": round(one_s, 3),
+                           "seq_tokens_per_s_per_layer": round(1 / one_s, 3),
+                           "sample": f"1 sequence of {one_tok} tokens, one run"}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
+              "not sharded across GPUs in this library.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_189_amd as pkv
+
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
+    if args.op == "sim":
+        sim_bench(args)
+        return
+    if args.op == "prefill":
+        prefill_bench(args)
+        return
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pkv.lib()
+    dev = torch.device("cuda:0")
+    ceiling = None if args.no_probe else read_ceiling(pkv, torch)
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
+    sink.add_(flush.sum())  # the zero fill's dirty lines drain here
+    log(f"workload {args.config} (headline)")
+    head = run_workload(args, args.config, args.partition, pkv, torch, flush, sink, True)
+    others = []
+    for idx in [int(x) for x in args.others.split(",") if x.strip() and x.strip() != "none"]:
+        if idx == args.config:
+            continue
+        log(f"workload {idx}")
+        others.append(run_workload(args, idx, -1, pkv, torch, flush, sink, False))
+    f = head["flushed"]
+    r = {"bound": "hbm", "kernel": "decode_partitions_kernel (pass 1)",
+         "achieved": f["pass1_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": f["pass1_frac"], "traffic": head["traffic"],
+         "bytes_per_launch": head["pass1_bytes_per_launch"], "avg_launch_us": f["pass1_us"],
+         "timed_launches": f["steps"],
+         "protocol": "each launch after a 1 GiB read that evicts L2 and MALL; HIP events on the "
+                     "launch stream",
+         "warm": {"achieved": head["warm"]["pass1_gbs"], "frac": head["warm"]["pass1_frac"],
+                  "avg_launch_us": head["warm"]["pass1_us"]}}
+    if ceiling:
+        r["ceiling"] = ceiling
+        r["ceiling_frac"] = round(f["pass1_gbs"] / ceiling["best_gbs"], 4)
+    parity_ok = all(x.get("parity", {}).get("ok", True) for x in [head] + others)
+    res = {
+        "metric": METRIC, "value": f["kv_gbs"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": f["step_ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic (seeded N(0,1) values, shuffled block tables)",
+        "config": {"workload": head["workload"], "seqs": head["seqs"],
+                   "q_heads": workloads_spec(head["index"]).num_q_heads,
+                   "kv_heads": workloads_spec(head["index"]).num_kv_heads,
+                   "head_dim": workloads_spec(head["index"]).head_dim,
+                   "block_size": head["block_size"], "partition_tokens": head["partition_tokens"],
+                   "mean_context": head["mean_context"], "parallelism": "1 GPU"},
+        "timing": "value and ms_per_step: mean over the timed steps of the step's HIP-event time "
+                  "(metadata copy to merge end), each step after a 1 GiB read that evicts L2 and "
+                  "MALL; warm: back-to-back steps, wall clock",
+        "seq_tokens_per_s_per_layer": f["seq_tokens_per_s_per_layer"],
+        "kv_bytes_per_step": head["kv_bytes_per_step"],
+        "kv_bytes_per_step_logical": head["kv_bytes_per_step_logical"],
+        "roofline": r,
+        "flushed": f, "warm": head["warm"], "step_kernels": head["step_kernels"],
+        "parity_max_err": head.get("parity", {}).get("max_err"),
+        "parity": head.get("parity"), "parity_ok_all": parity_ok,
+        "workloads": [summary(x) for x in [head] + others],
+        "setup_s": head["setup_s"],
+    }
+    if "cpu_baseline" in head:
+        res["cpu_baseline"] = head["cpu_baseline"]
     print(json.dumps(res), flush=True)
+    if not parity_ok:
+        print("bench.py: the GPU output of a timed state does not match the oracle", file=sys.stderr)
+        sys.exit(1)
+
+
+def workloads_spec(index):
+    import workloads
+    return workloads.SPECS[index]
+
+
+def summary(x):
+    """The per-workload figures kept in the line."""
+    keys = ("workload", "index", "seqs", "partition_tokens", "pass1_ranges", "mean_context",
+            "kv_bytes_per_step", "kv_bytes_per_step_logical", "pass1_bytes_per_launch", "traffic",
+            "dtype")
+    s = {k: x[k] for k in keys}
+    s["flushed"] = {k: x["flushed"][k] for k in ("step_ms", "step_ms_median", "step_ms_min",
+                                                 "kv_gbs", "seq_tokens_per_s_per_layer",
+                                                 "attention_us", "pass1_us", "pass1_gbs",
+                                                 "pass1_frac")}
+    s["warm"] = {k: x["warm"][k] for k in ("step_ms", "kv_gbs", "seq_tokens_per_s_per_layer",
+                                           "pass1_us", "pass1_frac")}
+    s["merge_us"] = x["step_kernels"]["merge_a7_us"]
+    s["append_us"] = x["step_kernels"]["append_a2_us"]
+    if "parity" in x:
+        s["parity"] = {k: x["parity"][k] for k in ("max_err", "kind", "tol", "lse_rel_err", "ok")}
+        s["parity"]["seqs"] = len(x["parity"]["seqs"])
+    return s
 
 
 MFMA_PEAK_TFLOPS = {0: 157.3, 1: 2500.0, 2: 2500.0}  # fp32 MFMA; bf16 MFMA (fp8 KV is widened to bf16)
@@ -499,58 +802,6 @@ def prefill_bench(args):
                         "traffic": None, "flops_per_launch": flops,
                         "avg_launch_us": round(ms * 1e3, 2)}}
     print(json.dumps(res), flush=True)
-
-
-def cpu_baseline(spec, w, bm, ids, args, pkv, torch):
-    """The fp64 oracle, untuned, on a bounded sample of the same workload:
-    its cache write stores each sampled sequence's decode token and its
-    attention runs over the sampled sequences.  Host copies of the sampled
-    sequences' blocks are made before the clock starts."""
-    from oracle import oracle as O
-    import workloads
-    BS = spec.block_size
-    k = min(args.cpu_seqs or CPU_SEQS[spec.index], len(ids))
-    seqs = np.arange(k)
-    _, tables, lens = bm.export(ids[:k])
-    n = [-(-int(L) // BS) for L in lens]
-    blocks = np.unique(np.concatenate([tables[i, :n[i]] for i in range(k)]))
-    remap = np.full(int(tables.max()) + 1, -1, dtype=np.int64)
-    remap[blocks] = np.arange(len(blocks))
-    t = np.full(tables.shape, -1, dtype=np.int32)
-    for i in range(k):
-        t[i, :n[i]] = remap[tables[i, :n[i]]]
-    idx = torch.from_numpy(blocks.astype(np.int64)).to(w.k_cache.device)
-
-    def host(x):
-        x = x.cpu()
-        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
-
-    kc, vc = host(w.k_cache.index_select(0, idx)), host(w.v_cache.index_select(0, idx))
-    q = np.ascontiguousarray(host(w.q[:k]))
-    kn = np.ascontiguousarray(host(w.k_new[:k]))
-    vn = np.ascontiguousarray(host(w.v_new[:k]))
-    pos = np.maximum(lens - 1, 0)  # the decode token of each sampled sequence
-    slots = np.array([t[i, pos[i] // BS] * BS + pos[i] % BS for i in range(k)], dtype=np.int64)
-    cores = len(os.sched_getaffinity(0))
-    if os.environ.get("OMP_NUM_THREADS", "").isdigit():  # the share this job was given
-        cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
-    reps = 0
-    t0 = time.perf_counter()
-    while True:  # repeat the sampled step until about 10 s of CPU work
-        O.reshape_and_cache(kn, vn, spec.q_dtype, kc, vc, spec.cache_dtype, slots, BS, w.k_scale,
-                            w.v_scale)
-        O.decode_attention(q, spec.q_dtype, kc, vc, spec.cache_dtype, t, lens, spec.num_kv_heads,
-                           BS, w.scale, w.k_scale, w.v_scale, threads=cores)
-        reps += 1
-        secs = time.perf_counter() - t0
-        if secs >= 10.0 or reps >= 50:
-            break
-    per_tok = 2 * spec.num_kv_heads * spec.head_dim * workloads.ELEM_BYTES[spec.cache_dtype]
-    kvb = int(np.sum(lens)) * per_tok * reps
-    return {"value": round(kvb / secs / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "seq_tokens_per_s_per_layer": round(k * reps / secs, 2), "seconds": round(secs, 2),
-            "sample": f"{k} of {len(ids)} sequences of one step (all {spec.num_q_heads} query heads, "
-                      f"{int(np.sum(lens))} tokens), cache write + fp64 attention, repeated {reps}x"}
 
 
 if __name__ == "__main__":

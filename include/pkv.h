@@ -475,6 +475,20 @@ const char* pkv_last_error(void);
 /* Library version string. */
 const char* pkv_version(void);
 
+/* Read-bandwidth probe, the measured ceiling beside the HBM peak: reads
+ * `bytes` (a positive multiple of 16) of device memory at buf (16-byte
+ * aligned).  mode 0: one contiguous sweep with the default cache policy;
+ * mode 1: the same with non-temporal loads; mode 2: `tiles` whole tiles of
+ * tile_bytes (a multiple of 1 KiB) in the order of the device int32 array
+ * `order` (tile ids, clamped into the buffer), non-temporal -- the access of
+ * a block-table walk over randomly placed blocks.  grid: workgroups of 256
+ * threads.  sink: device memory of grid * 256 uint32 (written only where a
+ * thread's folded data hits one fixed bit pattern by chance).  The caller
+ * times the launch. */
+pkv_status pkv_read_probe(const void* buf, int64_t bytes, int32_t mode, const int32_t* order,
+                          int64_t tile_bytes, int64_t tiles, uint32_t* sink, int32_t grid,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,7 +41,7 @@ EXPORTED = (
     "pkv_decode_partition_size", "pkv_decode_num_ranges", "pkv_decode_attention",
     "pkv_decode_attention_noalloc", "pkv_decode_attention_partitions",
     "pkv_decode_attention_merge", "pkv_prefill_attention", "pkv_sim_run", "pkv_status_string",
-    "pkv_last_error", "pkv_version",
+    "pkv_last_error", "pkv_version", "pkv_read_probe",
 )
 
 
@@ -140,6 +140,7 @@ def lib():
             "pkv_status_string": (C.c_char_p, [st]),
             "pkv_last_error": (C.c_char_p, []),
             "pkv_version": (C.c_char_p, []),
+            "pkv_read_probe": (st, [P, I64, I32, P, I64, I64, P, I32, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -408,6 +409,18 @@ def pkv_decode_attention_merge(params, out, context_lens, workspace=None, lse=No
     _check(lib().pkv_decode_attention_merge(
         C.byref(params), _ptr(out), _ptr(context_lens), wp, wb, _ptr(lse),
         _stream(stream, out)), "pkv_decode_attention_merge")
+
+
+def pkv_read_probe(buf: torch.Tensor, mode: int, sink: torch.Tensor,
+                   order: Optional[torch.Tensor] = None, tile_bytes: int = 0, grid: int = 0,
+                   stream=None):
+    """Read-bandwidth probe over buf (mode 0 sweep, 1 non-temporal sweep, 2
+    tiles in `order`); sink: int32 tensor of grid * 256 words."""
+    nbytes = buf.numel() * buf.element_size()
+    grid = grid or sink.numel() // 256
+    tiles = order.numel() if order is not None else 0
+    _check(lib().pkv_read_probe(_ptr(buf), nbytes, int(mode), _ptr(order), int(tile_bytes), tiles,
+                                _ptr(sink), int(grid), _stream(stream, buf)), "pkv_read_probe")
 
 
 def pkv_version() -> str:

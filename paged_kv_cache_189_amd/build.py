@@ -46,7 +46,7 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
                 print(" ".join(cmd), flush=True)
             subprocess.run(cmd, check=True)
 
-        for name in ("kernels", "decode_merge", "cache_write", "prefill"):
+        for name in ("kernels", "decode_merge", "cache_write", "prefill", "read_probe"):
             obj = os.path.join(tmp, name + ".o")
             run([hipcc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, name + ".hip"), "-o", obj])
             objs.append(obj)

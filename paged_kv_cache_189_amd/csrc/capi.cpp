@@ -477,4 +477,17 @@ pkv_status pkv_decode_attention_noalloc(const pkv_decode_params* p, void* out, c
   return check_hip(e, "decode_noalloc merge launch");
 }
 
+pkv_status pkv_read_probe(const void* buf, int64_t bytes, int32_t mode, const int32_t* order,
+                          int64_t tile_bytes, int64_t tiles, uint32_t* sink, int32_t grid, void* stream) {
+  if (!buf || !sink || !aligned(buf, 16) || !aligned(sink, 4))
+    return pkv_fail(PKV_ERR_INVALID_ARG, "read_probe: buf (16-byte aligned) and sink are required");
+  if (bytes <= 0 || bytes % 16 || grid <= 0 || grid > (1 << 20) || mode < 0 || mode > 2)
+    return pkv_fail(PKV_ERR_INVALID_ARG, "read_probe: bytes a positive multiple of 16, grid in [1, 2^20], mode 0..2");
+  if (mode == 2 && (!order || !aligned(order, 4) || tile_bytes <= 0 || tile_bytes % 1024 || tile_bytes > bytes ||
+                    tiles < 0))
+    return pkv_fail(PKV_ERR_INVALID_ARG, "read_probe: tiles need an order array and a tile size that is a multiple of 1 KiB");
+  return check_hip(pkv::launch_read_probe(buf, bytes, mode, order, tile_bytes, tiles, sink, grid, (hipStream_t)stream),
+                   "read_probe launch");
+}
+
 }  // extern "C"

@@ -108,6 +108,13 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, int cache_dtype, int he
 hipError_t launch_decode_merge(const DecodeArgs& a, int out_dtype, int head_dim,
                                hipStream_t stream, bool* supported);
 
+// Read-bandwidth probe (read_probe.hip): mode 0 contiguous sweep, 1 the same
+// non-temporal, 2 whole tiles in the order `order` (non-temporal); `grid`
+// workgroups of 256 threads; sink holds grid * 256 words.
+hipError_t launch_read_probe(const void* buf, int64_t bytes, int mode, const int32_t* order,
+                             int64_t tile_bytes, int64_t tiles, uint32_t* sink, int grid,
+                             hipStream_t stream);
+
 // Waves per workgroup of the partition kernel.
 constexpr int kWavesPerGroup = 4;
 // Upper bound of pass-1 workgroups (ranges); sizes the workspace.
