@@ -11,7 +11,7 @@ pass1_hbm_counters.json, which bench.py reads for `roofline.traffic` while the
 decode sources still hash to the value recorded there.
 
 Usage (on a machine with the GPU, from the repository root):
-    python profile_kernels.py [--decode 2:0,3:0,4:0,5:512] [--prefill 2:512,4:512]
+    python profile_kernels.py [--decode 4:0,2:0,3:0,5:512] [--prefill 2:512,4:512]
                               [--out DIR]
 and, where only the --out folder comes back from that machine, again with
 --from-output (and the same --out) to write the summaries from it.  rocprofv3 is started as a child
@@ -143,10 +143,34 @@ def stats_rows(d, top=8):
     return rows[:top] + [r for r in rows[top:] if "pkv::" in r["Name"]]
 
 
+def dispatch_times(d, name_part, flush_part="reduce_kernel", window=4):
+    """Durations (us) of the dispatches of kernels whose name holds name_part,
+    from the kernel trace, in dispatch order: (all, after_flush) -- the
+    second holds the dispatches with a flush kernel (name holding
+    flush_part) among the `window` dispatches before them (the flush's reduction and add, the
+    metadata copy, the cache write)."""
+    with open(one_csv(d, "kernel_trace.csv")) as f:
+        rows = list(csv.DictReader(f))
+    need = {"Kernel_Name", "Start_Timestamp", "End_Timestamp"}
+    if not rows or not need <= set(rows[0]):
+        raise SystemExit(f"unexpected kernel trace columns under {d}")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    every, flushed = [], []
+    for i, r in enumerate(rows):
+        if name_part not in r["Kernel_Name"]:
+            continue
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        every.append(us)
+        if any(flush_part in rows[j]["Kernel_Name"] for j in range(max(0, i - window), i)):
+            flushed.append(us)
+    return every, flushed
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--decode", default="2:0,3:0,4:0,5:512",
-                    help="decode workloads, config:partition_tokens")
+    ap.add_argument("--decode", default="4:0,2:0,3:0,5:512",
+                    help="decode workloads, config:partition_tokens (4:0, the default bench "
+                         "workload, is traced under the default bench command)")
     ap.add_argument("--prefill", default="2:512,4:512",
                     help="prefill workloads, config:chunk_tokens ('' for none)")
     ap.add_argument("--out", default="prof_out",
@@ -201,27 +225,33 @@ def main():
     for wl in [w for w in a.decode.split(",") if w]:
         cfg, part = (int(x) for x in wl.split(":"))
         tag = f"c{cfg}" + (f"p{part}" if part else "")
-        base = ["--", py, "-u", "bench.py", "--config", str(cfg), "--partition", str(part)]
+        base = ["--", py, "-u", "bench.py", "--config", str(cfg), "--partition", str(part),
+                "--others", "none", "--no-probe"]
         # the default workload is traced under exactly the default bench command
-        default = cfg == 2 and part == 0
+        default = cfg == 4 and part == 0
         trace_cmd = ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
                      f"{a.out}/{tag}/trace", "-o", "t"] + (
                      ["--", py, "-u", "bench.py"] if default else base + [
                          "--steps", "20", "--warmup", "3", "--no-cpu-baseline"])
         line = bench_line(run(trace_cmd, f"{a.out}/{tag}_trace.log", 300))
         rows = stats_rows(f"{a.out}/{tag}/trace")
+        # the pass-1 instance of this workload's cache dtype (the default
+        # command also runs the other workloads, in other instances)
+        inst = {2: "decode_partitions_kernel<1, 128", 3: "decode_partitions_kernel<1, 128",
+                4: "decode_partitions_kernel<2, 128", 5: "decode_partitions_kernel<1, 128"}[cfg]
+        every, flushed = dispatch_times(f"{a.out}/{tag}/trace", inst)
         got = {}
         pmc_cmds = []
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
             d = f"{a.out}/{tag}/{counter.split('_')[0].lower()}"
             cmd = ["rocprofv3", "--pmc", counter, "--kernel-include-regex", KERNEL,
                    "--output-format", "csv", "-d", d, "-o", "t"] + base + [
-                   "--steps", "5", "--warmup", "1", "--no-cpu-baseline"]
+                   "--steps", "5", "--warmup", "1", "--no-cpu-baseline", "--no-parity"]
             pmc_cmds.append(cmd)
             pl = bench_line(run(cmd, f"{a.out}/{tag}_{counter}.log", 300))
             v = per_dispatch(d, counter, KERNEL)
             got[counter] = (sum(v) / len(v), len(v), pl["roofline"]["bytes_per_launch"])
-        mbase = base + ["--steps", "5", "--warmup", "1", "--no-cpu-baseline"]
+        mbase = base + ["--steps", "5", "--warmup", "1", "--no-cpu-baseline", "--no-parity"]
         mcmds, mvals = metric_runs(a, tag, mbase, KERNEL, py)
         fetch_kib, nd, alg = got["FETCH_SIZE"]
         write_kib = got["WRITE_SIZE"][0]
@@ -235,8 +265,9 @@ def main():
                                  "fetch_kib": fetch_kib, "write_kib": write_kib,
                                  "summary": f"profiles/{fname}",
                                  "algorithmic_bytes_per_launch": int(alg)}
-        p1 = [r for r in rows if KERNEL in r["Name"]]
+        p1 = [r for r in rows if inst in r["Name"]]
         p1_us = float(p1[0]["AverageNs"]) / 1e3 if p1 else float("nan")
+        fl_us = sum(flushed) / len(flushed) if flushed else float("nan")
         r = line["roofline"]
         lines = [
             f"# Pass-1 kernel on {name}" + (f", split-KV partitions of {part} tokens" if part else ""),
@@ -257,9 +288,12 @@ def main():
         lines += [
             "",
             f"Under the profiler the bench line of this run read pass 1 at {r['avg_launch_us']} us "
-            f"(HIP events on the launch stream) against {p1_us:.1f} us average kernel time above; "
-            f"algorithmic bytes per launch {r['bytes_per_launch'] / 1e9:.4f} GB -> "
-            f"{r['achieved']} GB/s, {100 * r['frac']:.1f}% of 8 TB/s; whole step "
+            f"(mean of its {r['timed_launches']} timed launches, each after a 1 GiB read that "
+            f"evicts L2 and MALL; HIP events on the launch stream), against {fl_us:.1f} us mean "
+            f"kernel time of the {len(flushed)} pass-1 dispatches the trace shows right after that "
+            f"read, and {p1_us:.1f} us over all {len(every)} dispatches of this instance (warm "
+            f"steps included); algorithmic bytes per launch {r['bytes_per_launch'] / 1e9:.4f} GB "
+            f"-> {r['achieved']} GB/s, {100 * r['frac']:.1f}% of 8 TB/s; whole step "
             f"{line['ms_per_step']} ms.",
             "",
             "## HBM traffic of the pass-1 kernel",
@@ -291,7 +325,7 @@ def main():
         ]
         with open(os.path.join(PROFILES, fname), "w") as f:
             f.write("\n".join(lines))
-        log(f"{key}: pass 1 {p1_us:.1f} us, HBM {hbm / 1e9:.4f} GB vs algorithmic "
+        log(f"{key}: pass 1 {p1_us:.1f} us (after the flush {fl_us:.1f} us), HBM {hbm / 1e9:.4f} GB vs algorithmic "
             f"{alg / 1e9:.4f} GB ({hbm / alg:.3f}x) -> profiles/{fname}")
         with open(COUNTERS, "w") as f:
             json.dump(doc, f, indent=1)

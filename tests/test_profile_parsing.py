@@ -90,3 +90,30 @@ def test_short_names_drop_the_anonymous_namespace():
     n = "void pkv::(anonymous namespace)::decode_merge_rows_kernel<1, 128>(pkv::DecodeArgs)"
     assert P.short(n) == "void pkv::decode_merge_rows_kernel<1, 128>(pkv::DecodeArgs)"
     assert P.short("x" * 200).endswith("...") and len(P.short("x" * 200)) == 91
+
+
+TRACE_COLS = ["Kind", "Agent_Id", "Queue_Id", "Kernel_Id", "Kernel_Name", "Correlation_Id",
+              "Start_Timestamp", "End_Timestamp", "Grid_Size", "Workgroup_Size"]
+
+
+def test_dispatch_times_separates_launches_after_the_flush(tmp_path):
+    """Pass-1 dispatches with the flush's reduction among the four kernels
+    before them are the timed (flushed) launches; the trace lists kernels out
+    of start order, which the parser sorts."""
+    d = tmp_path / "trace"
+    d.mkdir()
+    p1 = "void pkv::decode_partitions_kernel<2, 128, 4, 3, true, 0>(pkv::DecodeArgs)"
+    seq = [("merge", 0, 10), ("cache_write_kernel", 10, 20), (p1, 20, 1020),      # warm
+           ("reduce_kernel<512>", 1100, 1300), ("add", 1300, 1301),
+           ("cache_write_kernel", 1310, 1320), (p1, 1320, 2420),                  # flushed
+           ("merge", 2420, 2430), ("cache_write_kernel", 2440, 2450), (p1, 2450, 3450)]
+    with open(d / "t_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=TRACE_COLS)
+        w.writeheader()
+        for name, a, b in reversed(seq):
+            r = {c: "0" for c in TRACE_COLS}
+            r.update(Kernel_Name=name, Start_Timestamp=str(a * 1000), End_Timestamp=str(b * 1000))
+            w.writerow(r)
+    every, flushed = P.dispatch_times(str(d), "decode_partitions_kernel<2, 128")
+    assert every == [1000.0, 1100.0, 1000.0]
+    assert flushed == [1100.0]
