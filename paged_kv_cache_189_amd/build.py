@@ -51,7 +51,7 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
             run([hipcc, *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, name + ".hip"), "-o", obj])
             objs.append(obj)
         cobj = os.path.join(tmp, "capi.o")
-        run([hipcc, "-x", "hip", *HIP_FLAGS, "-c", os.path.join(CSRC, "capi.cpp"), "-o", cobj])
+        run([hipcc, "-x", "hip", *HIP_FLAGS, *extra_flags, "-c", os.path.join(CSRC, "capi.cpp"), "-o", cobj])
         objs.append(cobj)
         for name in ("block_manager", "sim"):
             obj = os.path.join(tmp, name + ".o")
