@@ -313,8 +313,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
     }
   };
   // Raw scores of step u (past each row's causal bound -> -inf when MASK),
-  // their row max in log2 units, and whether it moves the running max.  The
-  // scale (> 0: a negative one was moved into Q) is applied inside the
+  // each lane's max of them, and whether some row's running max must move.
+  // The scale (> 0: a negative one was moved into Q) is applied inside the
   // exponent, p = 2^(s * scale - m).
   auto max_of = [&](const f32x4 (&sc)[NR][2], int u, auto masked, float (&x)[NR][8],
                     float (&mx)[NR], bool (&bump)[NR], bool live) {
@@ -334,11 +334,22 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       const float m23 = __builtin_amdgcn_fmed3f(x[k][2], x[k][3], pinf);
       const float m45 = __builtin_amdgcn_fmed3f(x[k][4], x[k][5], pinf);
       const float m67 = __builtin_amdgcn_fmed3f(x[k][6], x[k][7], pinf);
-      mx[k] = row_max(fmaxf(fmaxf(m01, m23), fmaxf(m45, m67)), pinf) * scl;
-      bump[k] = live && mx[k] > st[k].thr;  // always true on a row's first step; false for NaN
-      any = any || bump[k];
+      mx[k] = fmaxf(fmaxf(m01, m23), fmaxf(m45, m67));  // this lane's max; the row's below
+      // always true on a row's first step; false for NaN
+      any = any || (live && mx[k] * scl > st[k].thr);
     }
     return any;
+  };
+  // The row max across the 4 lanes of each row and which rows move their
+  // running max: needed only when some lane's own max passed its row's
+  // threshold (scl > 0 keeps the scaling monotone, so the row's scaled max
+  // passes it exactly when one of its lanes' does).
+  auto row_bumps = [&](float (&mx)[NR], bool (&bump)[NR], bool live) {
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      mx[k] = row_max(mx[k], pinf) * scl;
+      bump[k] = live && mx[k] > st[k].thr;
+    }
   };
   // Move the running max before a step's weights are formed; O must already
   // hold every earlier step.  Lanes without a bump rescale by 2^0 = 1.
@@ -434,8 +445,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       scores_of(kv[0], sc);
       float mx[NR];
       bool bump[NR];
-      if (__builtin_amdgcn_ballot_w64(max_of(sc, 0, std::true_type(), x, mx, bump, true)))
+      if (__builtin_amdgcn_ballot_w64(max_of(sc, 0, std::true_type(), x, mx, bump, true))) {
+        row_bumps(mx, bump, true);
         rescale(mx, bump);
+      }
     }
     int u = 0;
 #define PKV_PF_STAGE(J, MASK)                                                            \
@@ -453,7 +466,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
     float mx[NR];                                                                        \
     bool bump[NR];                                                                       \
     const bool any = max_of(scn, u + 1, std::integral_constant<bool, MASK>(), x, mx, bump, live); \
-    if (__builtin_amdgcn_ballot_w64(any)) rescale(mx, bump);                             \
+    if (__builtin_amdgcn_ballot_w64(any)) {                                              \
+      row_bumps(mx, bump, live);                                                         \
+      rescale(mx, bump);                                                                 \
+    }                                                                                    \
     ++u;                                                                                 \
   }
     // Stage u may skip masking when steps u and u + 1 are seen in full.
