@@ -238,7 +238,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   const char* kbase = static_cast<const char*>(a.k_cache) + ((int64_t)g * T::BYTES << shift);
   const char* vbase = static_cast<const char*>(a.v_cache) + ((int64_t)g * T::BYTES << shift);
   const int64_t bstride = (int64_t)a.num_kv_heads * T::BYTES << shift;
-  const int64_t last_block = a.num_blocks - 1;
+  // (table entries are int32, so the clamp runs in 32 bits, on the scalar unit)
+  const int last_block = a.num_blocks - 1 < INT32_MAX ? (int)(a.num_blocks - 1) : INT32_MAX;
   const int n16 = Lmax > 0 ? (Lmax + kBS - 1) / kBS : 0;  // 16-token tiles to read
   const int n32 = (n16 + 1) >> 1;                           // steps
   // Steps every row of the item sees in full (no causal masking needed).
@@ -263,8 +264,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       const int h = h0 + hh;
       int t16 = 2 * u + h;
       t16 = t16 < n16 - 1 ? t16 : n16 - 1;
-      int64_t phys = __builtin_amdgcn_readfirstlane(tbl[t16 >> shift]);
-      phys = phys < 0 ? 0 : (phys > last_block ? last_block : phys);
+      int p32 = __builtin_amdgcn_readfirstlane(tbl[t16 >> shift]);
+      p32 = p32 < 0 ? 0 : (p32 > last_block ? last_block : p32);
+      const int64_t phys = p32;
       const int half = t16 & ((1 << shift) - 1);
       const gchar_p kt = uniform_ptr(kbase + phys * bstride + half * (kBS * 16));
       const gchar_p vt = uniform_ptr(vbase + phys * bstride + half * (kBS * T::ES));
