@@ -42,7 +42,6 @@ import argparse
 import dataclasses
 import hashlib
 import json
-import math
 import os
 import re
 import sys

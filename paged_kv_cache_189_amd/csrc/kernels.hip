@@ -93,9 +93,9 @@ __device__ __forceinline__ void load_tile(Frags<KIND, D>& f, gchar_p kt, gchar_p
   }
 }
 
-// S^T[token 4*q4+i][head r] for i = 0..3.
-// Q^T fragments of one segment's query group, staged once in LDS and shared
-// by the NW waves: qf[j][lane] is the 16 bytes lane `lane` feeds to MFMA step j.
+// Q^T fragments of one segment's query group, staged once per segment in the
+// wave's own LDS slot: qf[j][lane] is the 16 bytes lane `lane` feeds to MFMA
+// step j.
 template <int KIND, int D>
 struct QLds {
   u32x4 qf[Tile<KIND, D>::NQ][64];
