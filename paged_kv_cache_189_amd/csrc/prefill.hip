@@ -25,49 +25,58 @@ namespace {
 // fragment as in decode; wave w owns NR consecutive query tiles.  Row r's
 // token sits at position p = L - C + j of its sequence and sees tokens 0..p
 // (causal); the workgroup walks the context up to its last row's position in
-// 32-token steps (two 16-token K/V tiles).  Each wave loads a quarter of every
-// step into registers PD steps ahead and publishes it to LDS (two buffers,
-// one barrier per step); all four waves run their query tiles against it, so
-// a K/V byte is fetched once per 4 * NR query tiles.  Rows past the chunk copy
-// the wave's last row and are not written; rows with p < 0 (chunk longer than
-// the context) are written as zeros.
+// 32-token steps (two 16-token K/V tiles).  A step is copied from the pool
+// straight into LDS (global_load_lds, 16 bytes a lane, no registers in
+// between), a quarter of it by each wave, PD + 1 steps ahead of its P.V, into
+// PD + 2 buffers with one barrier per step; all four waves run their query
+// tiles against it, so a K/V byte is fetched once per 4 * NR query tiles.
+// Rows past the chunk copy the wave's last row and are not written; rows with
+// p < 0 (chunk longer than the context) are written as zeros.
 //
 // Per step a row tile costs 2 x (D / 32) score MFMAs and D / 16 P.V MFMAs of
-// 16x16x32 (the two tiles' 4-token fragments of a lane form one 8-element
-// operand, so P.V runs at the full bf16 rate), against about 40 VALU
-// instructions of online softmax.  Steps every row of the item sees in full
+// 16x16x32.  The score MFMAs take the step's tokens in an order that leaves
+// each lane the scores of 8 consecutive tokens of its row, exactly the P
+// operand of one P.V MFMA, whose V operand is then 8 consecutive tokens of
+// one dim: 16 contiguous bytes of a pool V row.  About 40 VALU instructions
+// of online softmax go with them.  Steps every row of the item sees in full
 // take a loop with no causal masking.
 template <int KIND, int D>
 struct PrefillCfg {
   using T = Tile<KIND, D>;
   static constexpr int NR = KIND == kF32 ? 1 : 2;  // query tiles per wave
-  static constexpr int PD = 2;                      // 32-token steps in flight per wave
-  static constexpr int NWV = 4;                     // waves per workgroup (4 or 8)
-  static constexpr int HPW = 8 / NWV;               // 16-token tiles of a step each wave loads
-  // Each wave loads NL pieces of W bytes per lane of each 16-token K tile and
-  // as many of the V tile, so the four waves split a step evenly, unbranched.
-  static constexpr int W = T::BYTES / 256 < 16 ? T::BYTES / 256 : 16;
-  static constexpr int NL = T::BYTES / (256 * W);
-  static constexpr int FPC = W / T::VB;  // V fragments per loaded piece
-  static constexpr int PER_STEP = 2 * NL;  // pieces of K (and of V) per lane per step
-  static_assert(NL >= 1 && FPC >= 1, "tile split");
+  static constexpr int NWV = 4;                     // waves per workgroup
+  static constexpr int PD = 2;                      // steps in flight past the one scored next
+  static constexpr int NBUF = PD + 2;               // LDS step buffers
+  static constexpr int NC = T::BYTES / 1024;        // 1 KiB copies per 16-token tile
+  static constexpr int NCW = 4 * NC / NWV;          // copies per wave per step
+  static_assert(NCW >= 1 && (4 * NC) % NWV == 0, "step split");
+  static_assert(PD * NCW <= 63, "vmcnt range");
 };
 
-template <int KIND, int D>
-struct KVLds {  // one 16-token K/V tile in fragment order: [chunk][lane]
-  u32x4 k[Tile<KIND, D>::NK][64];
-  typename Tile<KIND, D>::V v[Tile<KIND, D>::NT][64];
-};
-
-// One 32-token step (tiles 2u and 2u + 1) in LDS.  K: per tile, fragment
-// order.  V: the two tiles' fragments of a lane side by side, v[nt][lane] =
-// {tile 2u, tile 2u + 1}, so one LDS read yields a P.V operand.
+// One 32-token step (tiles 2u and 2u + 1) in LDS, each tile as the pool holds
+// a 16-token block: K [D * ES / 16][16 tokens][16 bytes], V [D][16 tokens].
 template <int KIND, int D>
 struct PfStep {
-  using T = Tile<KIND, D>;
-  u32x4 k[2][T::NK][64];
-  typename T::V v[T::NT][64][2];
+  static constexpr int B = Tile<KIND, D>::BYTES;
+  u32x4 k[2][B / 16];
+  u32x4 v[2][B / 16];
 };
+
+// Copy 16 bytes a lane from global memory (base + voff) to LDS at lds + lane
+// * 16, tracked by vmcnt only.  Written as asm so the compiler, which does
+// not follow these copies by buffer, adds no wait of its own before every
+// LDS read: callers wait with vm_wait before the barrier that publishes a
+// step.  No output register: the copy writes only LDS.
+__device__ __forceinline__ void copy_to_lds(gchar_p base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
 
 template <int ES>
 struct ElemOf;
@@ -160,12 +169,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
                                              int s, int g, int item) {
   using T = Tile<KIND, D>;
   using C_ = PrefillCfg<KIND, D>;
-  using VT = typename T::V;
-  using PT = typename VecOf<C_::W>::T;
-  struct Parts {
-    VT p[C_::FPC];
-  };
-  constexpr int NR = C_::NR, PD = C_::PD, NL = C_::NL, W = C_::W, FPC = C_::FPC;
+  constexpr int NR = C_::NR, PD = C_::PD, NC = C_::NC, NCW = C_::NCW;
   constexpr int shift = SH;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, q4 = lane >> 4;
@@ -175,7 +179,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   int Ls = as_const(a.context_lens)[s];
   Ls = Ls < 0 ? 0 : (Ls > a.max_context_len ? a.max_context_len : Ls);
   const int per_wave = NQ * NR;
-  constexpr int NWV = C_::NWV, HPW = C_::HPW;
+  constexpr int NWV = C_::NWV;
   const int ibase = item * NWV * per_wave;             // first chunk token of the item
   const int ilast = (ibase + NWV * per_wave < C ? ibase + NWV * per_wave : C) - 1;
   const int Lmax = Ls - C + ilast + 1;                  // tokens the item's last row sees
@@ -191,18 +195,22 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   const uint32_t qflip = !qneg ? 0u : (KIND == kF32 ? 0x80000000u : 0x80008000u);
   int L[NR];
   bool row_ok[NR];
-  u32x4 q[NR][T::NQ];  // Q^T fragments, kept in registers for the whole item
-  {
-    constexpr int QES = KIND == kF32 ? 4 : 2;
+  gchar_p qrow[NR];
+  constexpr int QES = KIND == kF32 ? 4 : 2;
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      const int j = jbase + k * NQ + jl;
-      row_ok[k] = r < NQ * G && j <= jlast;
-      const int jj = row_ok[k] ? j : jfall;
-      const int Lrow = Ls - C + jj + 1;
-      L[k] = Lrow > 1 ? Lrow : 1;  // empty rows look at token 0, then write zeros
-      const gchar_p qrow = (gchar_p) static_cast<const char*>(a.q) +
-                           ((int64_t)(q0 + jj) * Hq + g * G + (r < NQ * G ? hh : 0)) * D * QES;
+  for (int k = 0; k < NR; ++k) {
+    const int j = jbase + k * NQ + jl;
+    row_ok[k] = r < NQ * G && j <= jlast;
+    const int jj = row_ok[k] ? j : jfall;
+    const int Lrow = Ls - C + jj + 1;
+    L[k] = Lrow > 1 ? Lrow : 1;  // empty rows look at token 0, then write zeros
+    qrow[k] = (gchar_p) static_cast<const char*>(a.q) +
+              ((int64_t)(q0 + jj) * Hq + g * G + (r < NQ * G ? hh : 0)) * D * QES;
+  }
+  u32x4 q[NR][T::NQ];  // Q^T fragments, kept in registers for the whole item
+  auto load_q = [&]() {
+#pragma unroll
+    for (int k = 0; k < NR; ++k)
 #pragma unroll
       for (int jq = 0; jq < T::NQ; ++jq) {
         int off;
@@ -210,34 +218,51 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
           off = ((jq >> 1) * 4 + q4) * 32 + (jq & 1) * 16;
         else
           off = (jq * 4 + q4) * 16;
-        q[k][jq] = *reinterpret_cast<gptr<u32x4>>(qrow + off) ^ qflip;
+        q[k][jq] = *reinterpret_cast<gptr<u32x4>>(qrow[k] + off) ^ qflip;
       }
-    }
-  }
+  };
 
-  // This lane's pieces of a 16-token tile: byte t of the tile in pool order
-  // lies at row * (row bytes << shift) + (t mod row bytes) from the tile's
-  // start (K rows are 16 tokens x 16 bytes, V rows 16 tokens of one dim).  K
-  // pieces land in LDS at t (pool order is fragment order); a V piece holds
-  // FPC 4-token fragments of dim d, stored to [d / 16][q4 * 16 + d % 16].
-  uint32_t ksrc[NL], kdst[NL], vsrc[NL], vdst[NL];
-  int vtok[NL];
+  // The copies of a step: 4 * NC of 1 KiB, copy idx = (kind * 2 + tile) *
+  // NC + c for K (kind 0) and V (kind 1) of tiles 2u, 2u + 1 and the tile's
+  // 1 KiB chunk c; wave w does idx = w + NWV * i.  With NC >= 4 copy i of
+  // every wave has kind and tile (i * NWV / NC) >> 1 and & 1; with NC < 4 a
+  // wave copies from the one tile (w / NC) & 1, of kind i (NC = 2) or w / 2
+  // (NC = 1).  A lane copies byte t = c * 1024 + lane * 16 of the tile in
+  // 16-token-block order, which a pool of 2^shift * 16-token blocks holds at
+  // row * (row bytes << shift) + (t mod row bytes) from the tile's start (K
+  // rows: 16 tokens x 16 bytes; V rows: the 16 tokens of one dim).
+  constexpr bool BOTH = NC >= 4;  // each wave copies from both tiles of a step
+  const int wtile = BOTH ? 0 : (w / NC) & 1;
+  const bool wkind = NC == 1 && (w >> 1);  // NC = 1: this wave's one copy is V
+  uint32_t csrc[NCW], cdst[NCW];
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const uint32_t t = (uint32_t)(((i * 4 + (w & 3)) * 64 + lane) * W);
-    ksrc[i] = ((t >> 8) << (8 + shift)) + (t & 255u);
-    kdst[i] = t;
-    constexpr uint32_t VR = 16u * T::ES;  // V row bytes of a tile
-    const uint32_t d = t / VR, tk = (t % VR) / T::ES;
-    vsrc[i] = d * (VR << shift) + t % VR;
-    vdst[i] = ((d >> 4) * 64u + (tk >> 2) * 16u + (d & 15u)) * (2 * T::VB);
-    vtok[i] = (int)tk;
+  for (int i = 0; i < NCW; ++i) {
+    const int idx = w + NWV * i, kh = idx / NC, c = idx % NC;
+    const uint32_t t = (uint32_t)(c * 1024 + lane * 16);
+    constexpr uint32_t VR = 16u * T::ES;  // V row bytes of a 16-token tile
+    const uint32_t ks = ((t >> 8) << (8 + shift)) + (t & 255u);
+    const uint32_t vs = t / VR * (VR << shift) + t % VR;
+    csrc[i] = kh >= 2 ? vs : ks;
+    cdst[i] = (uint32_t)(kh >> 1) * 2 * T::BYTES + (uint32_t)(kh & 1) * T::BYTES + (uint32_t)c * 1024;
   }
+  // LDS reads.  Score MFMA h takes step token 8 * (m / 4) + 4 * h + m % 4 as
+  // its row m, so lane (q4, r) gets the scores of step tokens 8 * q4 + 4 * h +
+  // i, i < 4: tokens 8 * q4 .. 8 * q4 + 7 of its row over h = 0, 1.  Its V
+  // operand is then V[tokens 8 * q4 ..][d], in tile q4 / 2 at token 8 * (q4 %
+  // 2) of the row of dim d.
+  uint32_t koff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int sg = 8 * (r >> 2) + 4 * h + (r & 3);
+    koff[h] = (uint32_t)((sg >> 4) * T::BYTES + q4 * 256 + (sg & 15) * 16);
+  }
+  const uint32_t voff = (uint32_t)(2 * T::BYTES + (q4 >> 1) * T::BYTES + r * 16 * T::ES + (q4 & 1) * 8 * T::ES);
 
   const cptr<int32_t> tbl = as_const(a.block_tables) + (int64_t)s * a.max_blocks;
   const char* kbase = static_cast<const char*>(a.k_cache) + ((int64_t)g * T::BYTES << shift);
   const char* vbase = static_cast<const char*>(a.v_cache) + ((int64_t)g * T::BYTES << shift);
-  const int64_t bstride = (int64_t)a.num_kv_heads * T::BYTES << shift;
+  // (the launcher refuses block strides of 2^32 bytes or more)
+  const uint32_t bstride = (uint32_t)a.num_kv_heads * (uint32_t)(T::BYTES << shift);
   // (table entries are int32, so the clamp runs in 32 bits, on the scalar unit)
   const int last_block = a.num_blocks - 1 < INT32_MAX ? (int)(a.num_blocks - 1) : INT32_MAX;
   const int n16 = Lmax > 0 ? (Lmax + kBS - 1) / kBS : 0;  // 16-token tiles to read
@@ -255,49 +280,49 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
 #pragma unroll
     for (int nt = 0; nt < T::NT; ++nt) st[k].acc.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // With 8 waves, waves 0-3 load the step's first tile and 4-7 its second.
-  const int h0 = HPW == 2 ? 0 : w >> 2;
-  PT sk[PD][HPW][NL], sv[PD][HPW][NL];
-  auto load_slot = [&](PT (&dk)[HPW][NL], PT (&dv)[HPW][NL], int u) {
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const int h = h0 + hh;
-      int t16 = 2 * u + h;
-      t16 = t16 < n16 - 1 ? t16 : n16 - 1;
-      int p32 = __builtin_amdgcn_readfirstlane(tbl[t16 >> shift]);
-      p32 = p32 < 0 ? 0 : (p32 > last_block ? last_block : p32);
-      const int64_t phys = p32;
-      const int half = t16 & ((1 << shift) - 1);
-      const gchar_p kt = uniform_ptr(kbase + phys * bstride + half * (kBS * 16));
-      const gchar_p vt = uniform_ptr(vbase + phys * bstride + half * (kBS * T::ES));
-      // Default cache policy: every item of the sequence reads these tiles,
-      // and the items of a (head, sequence) pair run side by side on one XCD.
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        dk[hh][i] = *reinterpret_cast<gptr<PT>>(kt + ksrc[i]);
-        dv[hh][i] = *reinterpret_cast<gptr<PT>>(vt + vsrc[i]);
-      }
-    }
+  // Table entries of the tiles of step j this wave copies from (past the
+  // context: its last tile).  Both tiles of a step share one entry when a
+  // block holds 32 tokens.
+  constexpr int NID = BOTH && shift == 0 ? 2 : 1;
+  auto tile_of = [&](int j, int h) {
+    const int t16 = 2 * j + h;
+    return t16 < n16 - 1 ? t16 : n16 - 1;
   };
-  // Publish a step to LDS.  On the step holding the sequence end V elements
-  // past Lmax are zeroed: their weights are 0 but the slots may hold NaN.
-  auto store_slot = [&](const PT (&dk)[HPW][NL], const PT (&dv)[HPW][NL], PfStep<KIND, D>& dst,
-                        int u, bool tail) {
+  auto ids_of = [&](int j, int (&id)[NID]) {
 #pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      const int h = h0 + hh;
-      char* kb = reinterpret_cast<char*>(dst.k[h]);
-      char* vb = reinterpret_cast<char*>(dst.v) + h * T::VB;
+    for (int h = 0; h < NID; ++h)
+      id[h] = __builtin_amdgcn_readfirstlane(tbl[(uint32_t)tile_of(j, BOTH ? h : wtile) >> shift]);
+  };
+  // Start the copies of step j into the LDS buffer at byte address lds.
+  // Default cache policy: every item of the sequence reads these tiles, and
+  // the items of a (head, sequence) pair run side by side on one XCD.
+  auto copy_step = [&](int j, const int (&id)[NID], uint32_t lds) {
+    constexpr int NT2 = BOTH ? 2 : 1;
+    const char* kt[NT2];
+    const char* vt[NT2];
 #pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        *reinterpret_cast<PT*>(kb + kdst[i]) = dk[hh][i];
-        PT v = dv[hh][i];
-        if (tail) v = zero_from<T::ES>(v, Lmax - (u * 2 + h) * kBS - vtok[i]);
-        const Parts pp = bitcast<Parts>(v);
+    for (int h = 0; h < NT2; ++h) {
+      const int t16 = tile_of(j, BOTH ? h : wtile);
+      const int e = id[NID == 2 ? h : 0];
+      const int p32 = e < 0 ? 0 : (e > last_block ? last_block : e);
+      const int half = t16 & ((1 << shift) - 1);
+      const uint64_t off = (uint64_t)(uint32_t)p32 * bstride;  // p32 >= 0
+      kt[h] = kbase + off + half * (kBS * 16);
+      vt[h] = vbase + off + half * (kBS * T::ES);
+    }
 #pragma unroll
-        for (int f = 0; f < FPC; ++f)
-          *reinterpret_cast<VT*>(vb + vdst[i] + f * 16 * (2 * T::VB)) = pp.p[f];
+    for (int i = 0; i < NCW; ++i) {
+      const char* src;
+      if constexpr (BOTH) {
+        constexpr int NWV_ = C_::NWV;
+        const int kh = i * NWV_ / NC;  // compile-time once unrolled
+        src = (kh >> 1) ? vt[kh & 1] : kt[kh & 1];
+      } else if constexpr (NC == 2) {
+        src = i ? vt[0] : kt[0];
+      } else {
+        src = wkind ? vt[0] : kt[0];
       }
+      copy_to_lds(uniform_ptr(src), csrc[i], lds + cdst[i]);
     }
   };
 
@@ -305,11 +330,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   constexpr int NPB = KIND == kF32 ? 2 : 1;
   // S^T of a step for every row tile, from the step's K in LDS.
   auto scores_of = [&](const PfStep<KIND, D>& t, f32x4 (&sc)[NR][2]) {
+    const char* kb = reinterpret_cast<const char*>(t.k);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       u32x4 kf[T::NK];
 #pragma unroll
-      for (int j = 0; j < T::NK; ++j) kf[j] = t.k[h][j][lane];
+      for (int j = 0; j < T::NK; ++j) kf[j] = *reinterpret_cast<const u32x4*>(kb + koff[h] + j * 1024);
 #pragma unroll
       for (int k = 0; k < NR; ++k) sc[k][h] = pf_scores<KIND, D>(kf, q[k]);
     }
@@ -329,7 +355,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = sc[k][h][i];
-          if (MASK) v = u * 2 * kBS + h * kBS + 4 * q4 + i < L[k] ? v : -INFINITY;
+          if (MASK) v = u * 2 * kBS + 8 * q4 + 4 * h + i < L[k] ? v : -INFINITY;
           x[k][h * 4 + i] = v;
         }
       const float m01 = __builtin_amdgcn_fmed3f(x[k][0], x[k][1], pinf);
@@ -367,7 +393,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       for (int nt = 0; nt < T::NT; ++nt) st[k].acc.o[nt] *= alpha;
     }
   };
-  // Weights of a step, summed into l (fp32) and packed as P.V operands.
+  // Weights of a step, summed into l (fp32) and packed as P.V operands:
+  // p[e] is the weight of step token 8 * q4 + e.
   auto weights_of = [&](const float (&x)[NR][8], auto masked, PB (&pw)[NR][NPB]) {
     constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
@@ -393,12 +420,36 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       }
     }
   };
-  // O^T[d][row] += V^T . P^T over a step's 32 tokens.
-  auto pv_of = [&](const PfStep<KIND, D>& t, const PB (&pw)[NR][NPB]) {
+  // A lane's V operands of a step: for each 16-dim tile, V[tokens 8 * q4 ..
+  // 8 * q4 + 7][d] (fp32: two halves of 4 tokens).  Read ahead of their use
+  // so the stage's softmax work covers the LDS latency.
+  using VR = typename std::conditional<KIND == kBF16, u32x4, typename std::conditional<KIND == kFP8, u32x2, u32x4>::type>::type;
+  constexpr int NVR = KIND == kF32 ? 2 * T::NT : T::NT;
+  auto read_v = [&](const PfStep<KIND, D>& t, VR (&vr)[NVR]) {
+    const char* vb = reinterpret_cast<const char*>(t.k) + voff;  // V follows K in the step
 #pragma unroll
     for (int nt = 0; nt < T::NT; ++nt) {
-      const VT va = t.v[nt][lane][0], vb = t.v[nt][lane][1];
       if constexpr (KIND == kF32) {
+        vr[2 * nt] = *reinterpret_cast<const u32x4*>(vb + nt * 16 * 64);
+        vr[2 * nt + 1] = *reinterpret_cast<const u32x4*>(vb + nt * 16 * 64 + 16);
+      } else {
+        vr[nt] = *reinterpret_cast<const VR*>(vb + nt * 16 * 16 * T::ES);
+      }
+    }
+  };
+  // O^T[d][row] += V^T . P^T over the 32 tokens of step u.  On the step
+  // holding the end of what the item reads, V past Lmax is zeroed: those
+  // weights are 0 but the slots may hold NaN.
+  auto pv_of = [&](const VR (&vr)[NVR], const PB (&pw)[NR][NPB], int u, bool tail) {
+    const int lim = Lmax - (u * 2 * kBS + 8 * q4);  // valid tokens of this lane's 8
+#pragma unroll
+    for (int nt = 0; nt < T::NT; ++nt) {
+      if constexpr (KIND == kF32) {
+        u32x4 va = vr[2 * nt], vc = vr[2 * nt + 1];
+        if (tail) {
+          va = zero_from<4>(va, lim);
+          vc = zero_from<4>(vc, lim - 4);
+        }
 #pragma unroll
         for (int k = 0; k < NR; ++k) {
           f32x4 o = st[k].acc.o[nt];
@@ -407,41 +458,55 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
             o = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(va[i]), pw[k][0][i], o, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            o = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vb[i]), pw[k][1][i], o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(vc[i]), pw[k][1][i], o, 0, 0, 0);
           st[k].acc.o[nt] = o;
         }
       } else {
-        u32x2 lo, hi;
+        VR v = vr[nt];
+        if (tail) v = zero_from<T::ES>(v, lim);
+        u32x4 vv;
         if constexpr (KIND == kBF16) {
-          lo = va;
-          hi = vb;
+          vv = v;
         } else {
-          lo = bitcast<u32x2>(fp8x4_to_bf16x4(va));
-          hi = bitcast<u32x2>(fp8x4_to_bf16x4(vb));
+          const u32x2 lo = bitcast<u32x2>(fp8x4_to_bf16x4(v[0]));
+          const u32x2 hi = bitcast<u32x2>(fp8x4_to_bf16x4(v[1]));
+          vv = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
-        const bf16x8 vv = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
         for (int k = 0; k < NR; ++k)
-          st[k].acc.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pw[k][0], st[k].acc.o[nt], 0, 0, 0);
+          st[k].acc.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(vv), pw[k][0], st[k].acc.o[nt], 0, 0, 0);
       }
     }
   };
 
   if (n32 > 0) {
-    // Software pipeline over steps.  Stage u publishes step u + 1 and runs
-    // the MFMAs of step u + 1's scores and step u's P.V while the VALU forms
-    // step u's weights and step u + 1's row max, so matrix and vector work
-    // of one wave overlap.  Step j lives in LDS buffer j mod 3: stage u reads
-    // buffers u and u + 1 and writes u + 1, last read at stage u - 2 (before
-    // the previous stage's barrier), so one barrier per stage suffices.
-    // Register slot j mod PD holds step j from its load, issued PD stages
-    // ahead, until it is published.
+    // Software pipeline over steps.  Stage u runs the MFMAs of step u + 1's
+    // scores and step u's P.V while the VALU forms step u's weights and step
+    // u + 1's row max, so matrix and vector work of one wave overlap.  Step j
+    // lives in LDS buffer j mod (PD + 2); its copies start right after the
+    // barrier of stage j - PD - 1, into the buffer of step j - PD - 2, whose
+    // last reads (stage j - PD - 2) precede that barrier.  Before the barrier
+    // of stage u each wave waits for its own copies of step u + 1; those of
+    // the PD - 1 steps after it stay in flight.
+    constexpr uint32_t SB = sizeof(PfStep<KIND, D>);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)kv;  // LDS byte address of buffer 0
     float x[NR][8];
+    int id[NID];
+    // Step 0's copies and Q's loads overlap; an explicit wait that the
+    // compiler sees then retires both, so its own wait for Q (it does not
+    // count the asm copies) cannot later hold the copies of steps 1..PD.
+    ids_of(0, id);
+    copy_step(0, id, lds0);
+    load_q();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt, lgkmcnt unchecked
 #pragma unroll
-    for (int i = 0; i < PD; ++i) load_slot(sk[i], sv[i], i);
-    store_slot(sk[0], sv[0], kv[0], 0, 2 * kBS > Lmax);
+    for (int j = 1; j <= PD; ++j) {
+      ids_of(j, id);
+      copy_step(j, id, lds0 + j * SB);
+    }
+    ids_of(PD + 1, id);
+    vm_wait<PD * NCW>();
     __syncthreads();
-    load_slot(sk[0], sv[0], PD);
     {
       f32x4 sc[NR][2];
       scores_of(kv[0], sc);
@@ -455,16 +520,20 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
     int u = 0;
 #define PKV_PF_STAGE(J, MASK)                                                            \
   {                                                                                      \
-    constexpr int BC = (J) % 3, BN = ((J) + 1) % 3, SL = ((J) + 1) % PD;                 \
+    constexpr int NB = C_::NBUF;                                                         \
+    constexpr int BC = (J) % NB, BN = ((J) + 1) % NB, BI = ((J) + PD + 1) % NB;          \
     const bool live = u + 1 < n32;                                                       \
-    store_slot(sk[SL], sv[SL], kv[BN], u + 1, MASK && (u + 2) * 2 * kBS > Lmax);         \
+    vm_wait<(PD - 1) * NCW>();                                                           \
     __syncthreads();                                                                     \
-    load_slot(sk[SL], sv[SL], u + 1 + PD);                                               \
+    copy_step(u + PD + 1, id, lds0 + BI * SB);                                           \
+    ids_of(u + PD + 2, id);                                                              \
+    VR vr[NVR];                                                                          \
+    read_v(kv[BC], vr);                                                                  \
     f32x4 scn[NR][2];                                                                    \
     scores_of(kv[BN], scn);                                                              \
     PB pw[NR][NPB];                                                                      \
     weights_of(x, std::integral_constant<bool, MASK>(), pw);                             \
-    pv_of(kv[BC], pw);                                                                   \
+    pv_of(vr, pw, u, MASK && (u + 1) * 2 * kBS > Lmax);                                  \
     float mx[NR];                                                                        \
     bool bump[NR];                                                                       \
     const bool any = max_of(scn, u + 1, std::integral_constant<bool, MASK>(), x, mx, bump, live); \
@@ -475,18 +544,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
     ++u;                                                                                 \
   }
     // Stage u may skip masking when steps u and u + 1 are seen in full.
-    constexpr int U = PD % 3 == 0 ? PD : 3 * PD;  // stages per unrolled round
+    constexpr int U = C_::NBUF;  // stages per unrolled round
+    static_assert(U == 4, "the stage loops below are written for 4 stages a round");
     const int u_plain = u_full >= 1 ? (u_full - 1) / U * U : 0;
-    static_assert(U <= 6, "the stage loops below are written for 6 stages a round");
     while (u < u_plain) {
       PKV_PF_STAGE(0, false)
       PKV_PF_STAGE(1, false)
       PKV_PF_STAGE(2, false)
-      if constexpr (U == 6) {
-        PKV_PF_STAGE(3, false)
-        PKV_PF_STAGE(4, false)
-        PKV_PF_STAGE(5, false)
-      }
+      PKV_PF_STAGE(3, false)
     }
     for (;;) {
       PKV_PF_STAGE(0, true)
@@ -495,16 +560,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       if (u >= n32) break;
       PKV_PF_STAGE(2, true)
       if (u >= n32) break;
-      if constexpr (U == 6) {
-        PKV_PF_STAGE(3, true)
-        if (u >= n32) break;
-        PKV_PF_STAGE(4, true)
-        if (u >= n32) break;
-        PKV_PF_STAGE(5, true)
-        if (u >= n32) break;
-      }
+      PKV_PF_STAGE(3, true)
+      if (u >= n32) break;
     }
 #undef PKV_PF_STAGE
+    // No copy may still be writing LDS when the workgroup ends.
+    vm_wait<0>();
   }
 
 #pragma unroll
@@ -546,7 +607,7 @@ template <int KIND, int D, int SH>
 __global__ __launch_bounds__((64 * PrefillCfg<KIND, D>::NWV)) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int NR = PrefillCfg<KIND, D>::NR;
-  __shared__ PfStep<KIND, D> kv[3];
+  __shared__ PfStep<KIND, D> kv[PrefillCfg<KIND, D>::NBUF];
   __shared__ int lct[kPrefillMaxSeqs + 1];
   constexpr int NWV = PrefillCfg<KIND, D>::NWV;
   __shared__ int wsums[NWV];
@@ -594,7 +655,10 @@ hipError_t launch_prefill(const PrefillArgs& a, int cache, int D, int64_t num_ro
   const int64_t items = (num_rows + per - 1) / per + a.num_seqs;
   int64_t groups = (int64_t)a.num_kv_heads * items;
   groups = (groups + 7) / 8 * 8;
-  if (groups > INT32_MAX) {
+  // the kernel computes block offsets as 32-bit stride x 32-bit block id
+  const int64_t es = cache == kF32 ? 4 : (cache == kBF16 ? 2 : 1);
+  const int64_t block_stride = ((int64_t)a.num_kv_heads * kBS * D * es) << a.block_shift;
+  if (groups > INT32_MAX || block_stride > (int64_t)UINT32_MAX) {
     *supported = false;
     return hipSuccess;
   }
