@@ -53,12 +53,19 @@ struct PrefillCfg {
   static_assert(PD * NCW <= 63, "vmcnt range");
 };
 
-// One 32-token step (tiles 2u and 2u + 1) in LDS, each tile as the pool holds
-// a 16-token block: K [D * ES / 16][16 tokens][16 bytes], V [D][16 tokens].
+// One 32-token step (tiles 2u and 2u + 1) in LDS, in 16-byte units.  K: each
+// tile as the pool holds a 16-token block, [D * ES / 16][16 tokens][16 bytes],
+// the second tile 64 bytes further on, so a read of tokens of both tiles by 16
+// lanes spreads over all banks.  V: unit (d, u) = V[tokens 16 * u / ES ..][d]
+// (ES bytes a token, 16 / ES tokens a unit) at unit index ((d / 16) * ES + u) *
+// 16 + d % 16 of its tile, so the units of one u and 16 consecutive d -- what
+// 16 lanes of a P.V operand read -- are 256 contiguous bytes.
 template <int KIND, int D>
 struct PfStep {
   static constexpr int B = Tile<KIND, D>::BYTES;
-  u32x4 k[2][B / 16];
+  static constexpr int KPAD = 64;
+  static constexpr int VOFS = 2 * B + KPAD;  // V's first byte
+  u32x4 k[(2 * B + KPAD) / 16];
   u32x4 v[2][B / 16];
 };
 
@@ -68,8 +75,9 @@ struct PfStep {
 // LDS read: callers wait with vm_wait before the barrier that publishes a
 // step.  No output register: the copy writes only LDS.
 __device__ __forceinline__ void copy_to_lds(gchar_p base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(lds)
-               : "memory", "m0");
+  // (lds is wave-uniform; readfirstlane keeps it in a scalar register)
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base),
+               "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -227,10 +235,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   // 1 KiB chunk c; wave w does idx = w + NWV * i.  With NC >= 4 copy i of
   // every wave has kind and tile (i * NWV / NC) >> 1 and & 1; with NC < 4 a
   // wave copies from the one tile (w / NC) & 1, of kind i (NC = 2) or w / 2
-  // (NC = 1).  A lane copies byte t = c * 1024 + lane * 16 of the tile in
-  // 16-token-block order, which a pool of 2^shift * 16-token blocks holds at
-  // row * (row bytes << shift) + (t mod row bytes) from the tile's start (K
-  // rows: 16 tokens x 16 bytes; V rows: the 16 tokens of one dim).
+  // (NC = 1).  A lane copies LDS unit c * 64 + lane of the tile (the step
+  // layout above); a pool of 2^shift * 16-token blocks holds a tile's row
+  // (K: 16 tokens x 16 bytes of one dim group; V: the 16 tokens of one dim)
+  // at row * (row bytes << shift) from the tile's start.
   constexpr bool BOTH = NC >= 4;  // each wave copies from both tiles of a step
   const int wtile = BOTH ? 0 : (w / NC) & 1;
   const bool wkind = NC == 1 && (w >> 1);  // NC = 1: this wave's one copy is V
@@ -238,25 +246,28 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
 #pragma unroll
   for (int i = 0; i < NCW; ++i) {
     const int idx = w + NWV * i, kh = idx / NC, c = idx % NC;
-    const uint32_t t = (uint32_t)(c * 1024 + lane * 16);
+    const uint32_t t = (uint32_t)(c * 1024 + lane * 16), un = t / 16;
     constexpr uint32_t VR = 16u * T::ES;  // V row bytes of a 16-token tile
     const uint32_t ks = ((t >> 8) << (8 + shift)) + (t & 255u);
-    const uint32_t vs = t / VR * (VR << shift) + t % VR;
+    const uint32_t vd = un / (16 * T::ES) * 16 + un % 16, vu = un / 16 % T::ES;
+    const uint32_t vs = vd * (VR << shift) + vu * 16;
     csrc[i] = kh >= 2 ? vs : ks;
-    cdst[i] = (uint32_t)(kh >> 1) * 2 * T::BYTES + (uint32_t)(kh & 1) * T::BYTES + (uint32_t)c * 1024;
+    cdst[i] = (kh >= 2 ? (uint32_t)PfStep<KIND, D>::VOFS + (uint32_t)(kh & 1) * T::BYTES
+                       : (uint32_t)(kh & 1) * (T::BYTES + PfStep<KIND, D>::KPAD)) + (uint32_t)c * 1024;
   }
   // LDS reads.  Score MFMA h takes step token 8 * (m / 4) + 4 * h + m % 4 as
   // its row m, so lane (q4, r) gets the scores of step tokens 8 * q4 + 4 * h +
   // i, i < 4: tokens 8 * q4 .. 8 * q4 + 7 of its row over h = 0, 1.  Its V
-  // operand is then V[tokens 8 * q4 ..][d], in tile q4 / 2 at token 8 * (q4 %
-  // 2) of the row of dim d.
+  // operand is then V[tokens 8 * q4 ..][d], in tile q4 / 2 from token 8 * (q4
+  // % 2): unit u = (q4 % 2) * ES / 2 of dim d (fp8: half of unit 0).
   uint32_t koff[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int sg = 8 * (r >> 2) + 4 * h + (r & 3);
-    koff[h] = (uint32_t)((sg >> 4) * T::BYTES + q4 * 256 + (sg & 15) * 16);
+    koff[h] = (uint32_t)((sg >> 4) * (T::BYTES + PfStep<KIND, D>::KPAD) + q4 * 256 + (sg & 15) * 16);
   }
-  const uint32_t voff = (uint32_t)(2 * T::BYTES + (q4 >> 1) * T::BYTES + r * 16 * T::ES + (q4 & 1) * 8 * T::ES);
+  const uint32_t voff = (uint32_t)(PfStep<KIND, D>::VOFS + (q4 >> 1) * T::BYTES +
+                                   (KIND == kFP8 ? r * 16 + (q4 & 1) * 8 : ((q4 & 1) * T::ES / 2 * 16 + r) * 16));
 
   const cptr<int32_t> tbl = as_const(a.block_tables) + (int64_t)s * a.max_blocks;
   const char* kbase = static_cast<const char*>(a.k_cache) + ((int64_t)g * T::BYTES << shift);
@@ -429,11 +440,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
     const char* vb = reinterpret_cast<const char*>(t.k) + voff;  // V follows K in the step
 #pragma unroll
     for (int nt = 0; nt < T::NT; ++nt) {
-      if constexpr (KIND == kF32) {
-        vr[2 * nt] = *reinterpret_cast<const u32x4*>(vb + nt * 16 * 64);
-        vr[2 * nt + 1] = *reinterpret_cast<const u32x4*>(vb + nt * 16 * 64 + 16);
+      if constexpr (KIND == kF32) {  // units u and u + 1: 4 tokens each
+        vr[2 * nt] = *reinterpret_cast<const u32x4*>(vb + nt * 256 * T::ES);
+        vr[2 * nt + 1] = *reinterpret_cast<const u32x4*>(vb + nt * 256 * T::ES + 256);
       } else {
-        vr[nt] = *reinterpret_cast<const VR*>(vb + nt * 16 * 16 * T::ES);
+        vr[nt] = *reinterpret_cast<const VR*>(vb + nt * 256 * T::ES);
       }
     }
   };
