@@ -17,7 +17,9 @@ import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpkv.so")
+# PKV_LIB names another build of the library (a variant built with
+# `python -m paged_kv_cache_189_amd.build --define ... --out ...`).
+LIB_PATH = os.environ.get("PKV_LIB") or os.path.join(HERE, "libpkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID_ARG = -1

@@ -64,4 +64,13 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="a preprocessor definition for every HIP compile (for example "
+                         "PKV_DECODE_VALU_SCORES=1, the vector-unit q.K variant of decode)")
+    ap.add_argument("--out", default=LIB, help="library path (default: next to this file)")
+    args = ap.parse_args()
+    print(build(verbose=args.verbose, extra_flags=[f"-D{d}" for d in args.define], out=args.out))

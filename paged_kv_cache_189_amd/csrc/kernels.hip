@@ -99,6 +99,9 @@ __device__ __forceinline__ void load_tile(Frags<KIND, D>& f, gchar_p kt, gchar_p
 template <int KIND, int D>
 struct QLds {
   u32x4 qf[Tile<KIND, D>::NQ][64];
+#if PKV_DECODE_VALU_SCORES
+  float sx[16][16];  // scores S[head][token] of the tile, vector-unit variant
+#endif
 };
 
 // S^T[token 4*q4+i][head r] for i = 0..3.
@@ -129,6 +132,55 @@ __device__ __forceinline__ f32x4 scores(const Frags<KIND, D>& f, const QLds<KIND
   }
   return acc;
 }
+
+// The q.K contraction on the vector unit instead of the matrix cores, for
+// the comparison that decides which unit runs it (built with
+// -DPKV_DECODE_VALU_SCORES=1; the 16-token tile path of bf16 and fp8 caches;
+// 32-token blocks and fp8 block pairs keep MFMA).  Lane (t, c) holds token
+// t's K dims in the chunks of MFMA step j (the same dims lane (h, c) holds of
+// head h's Q); it dots them with every head's Q chunk read from the wave's
+// LDS slot (v_dot2_f32_bf16, fp32 accumulation), the four lanes of a token
+// add their parts, and the scores go through LDS to the layout scores()
+// returns: S^T[token 4 q4 + i][head r], zero for the padding rows r >= G.
+// The result differs from the MFMA one only in fp32 summation order.
+#ifndef PKV_DECODE_VALU_SCORES
+#define PKV_DECODE_VALU_SCORES 0
+#endif
+#if PKV_DECODE_VALU_SCORES
+__device__ __forceinline__ float sum_across_groups(float v);
+template <int KIND, int D>
+__device__ __forceinline__ f32x4 scores_valu(const Frags<KIND, D>& f, QLds<KIND, D>& q, int lane, int G) {
+  using T = Tile<KIND, D>;
+  static_assert(KIND != kF32, "fp32 keeps the MFMA contraction");
+  const int t = lane & 15, c = lane >> 4;
+  u32x4 kb[T::NQ];  // token t's K as bf16 pairs, chunk jq as Q fragment jq
+  if constexpr (KIND == kBF16) {
+#pragma unroll
+    for (int j = 0; j < T::NK; ++j) kb[j] = f.k[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < T::NK; ++j) fp8x16_to_bf16(f.k[j], kb[2 * j], kb[2 * j + 1]);
+  }
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    if (h >= G) break;  // wave-uniform
+    float acc = 0.f;
+#pragma unroll
+    for (int jq = 0; jq < T::NQ; ++jq) {
+      const u32x4 qv = q.qf[jq][h + 16 * c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_fdot2_f32_bf16(bitcast<bf16x2>(kb[jq][e]), bitcast<bf16x2>(qv[e]), acc, false);
+    }
+    acc = sum_across_groups(acc);  // the four dim quarters of token t
+    if ((h & 3) == c) q.sx[h][t] = acc;
+  }
+  // A wave's LDS accesses complete in order: the row is the one just written.
+  const int r = lane & 15, q4 = lane >> 4;
+  const f32x4 v = *reinterpret_cast<const f32x4*>(&q.sx[r][4 * q4]);
+  return r < G ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+#endif
 
 // The lane's four weights P as multiplied into V: bf16 (round to nearest
 // even) except on the fp32 path.
@@ -235,10 +287,19 @@ struct RunState {
 // masking uses the sequence bound only.
 template <int KIND, int D>
 __device__ __forceinline__ void process_block(RunState<KIND, D>& st, const Frags<KIND, D>& f,
-                                              const QLds<KIND, D>& q, int b, int L, int Lv,
-                                              float score_scale_log2, int lane, int q4) {
+                                              QLds<KIND, D>& q, int b, int L, int Lv,
+                                              float score_scale_log2, int lane, int q4, int G) {
   using T = Tile<KIND, D>;
+#if PKV_DECODE_VALU_SCORES
+  f32x4 sc;
+  if constexpr (KIND == kF32)
+    sc = scores<KIND, D>(f, q, lane);
+  else
+    sc = scores_valu<KIND, D>(f, q, lane, G);
+#else
+  (void)G;
   const f32x4 sc = scores<KIND, D>(f, q, lane);
+#endif
   const int tok0 = b * kBS + 4 * q4;
   float x[4];
   bool valid[4];
@@ -799,7 +860,7 @@ __device__ __forceinline__ void decode_segment(const DecodeArgs& a, QLds<KIND, D
   load_tile<KIND, D, STR>(BUF, kt, vt, toff);
 #define PKV_STAGE(CUR, NXT)                                              \
   PKV_PREFETCH(NXT, S - 1)                                               \
-  process_block<KIND, D>(st, CUR, qs, b, L, L, a.score_scale_log2, lane, q4); \
+  process_block<KIND, D>(st, CUR, qs, b, L, L, a.score_scale_log2, lane, q4, G); \
   pace(done + (b - b_begin), total);                                     \
   b += NW;                                                               \
   if (b < b_end && --to_cut == 0) {                                      \
