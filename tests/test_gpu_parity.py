@@ -123,6 +123,23 @@ def test_partition_cuts_odd_and_even_tiles(cache, part):
 
 
 @pytest.mark.parametrize("cache", [BF16, E4M3])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("group", [1, 4, 16])
+def test_many_cuts_per_wave(cache, D, group):
+    """One-tile partitions over ~20 000 tiles: every pass-1 range holds about
+    ten cuts, so each wave stages its partial states in LDS, writes them out
+    whenever its staging area is full (every three cuts at D = 128, two at
+    D = 64) and once more at its range's end; G = 1 and 4 leave staged rows
+    that must not be written."""
+    lens = [40_000, 39_001, 20_017, 41_000, 1, 17]
+    base = {BF16: 2, E4M3: 4}[cache]
+    spec = small_spec(260 + 10 * group + D // 64 + cache, base, len(lens), 2 * group, 2, D,
+                      lens, cache)
+    c = G.build(spec, partition_size=16)
+    full_parity(c, label=f"many cuts dtype={cache} D={D} G={group}")
+
+
+@pytest.mark.parametrize("cache", [BF16, E4M3])
 @pytest.mark.parametrize("part", [0, 64])
 def test_more_than_1024_sequences(cache, part):
     """A batch past the in-kernel plan's 1024 sequences: a one-workgroup plan
