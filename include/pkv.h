@@ -386,8 +386,10 @@ pkv_status pkv_decode_attention_noalloc(const pkv_decode_params* p, void* out, c
  * = 0 and query_start[num_seqs] = num_query_tokens (not checked: it lives
  * on the device).  Other fields, dtypes and limits as pkv_decode_params;
  * num_seqs <= 1024; scale may be any finite number (negative and zero
- * included).  No workspace: a workgroup takes a (kv head, sequence, run of
- * query tokens) and walks the table up to its last row's position.
+ * included).  PKV_ERR_UNSUPPORTED also when a physical block of all kv heads
+ * (num_kv_heads * block_size * head_dim * element bytes) reaches 4 GiB.  No
+ * workspace: a workgroup takes a (kv head, sequence, run of query tokens) and
+ * walks the table up to its last row's position.
  * Rounding: bf16 and fp8 caches multiply bf16-rounded weights into V and
  * normalise by the fp32 sum of the weights. */
 typedef struct {

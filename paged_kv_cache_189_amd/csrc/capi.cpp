@@ -412,7 +412,10 @@ pkv_status pkv_prefill_attention(const pkv_prefill_params* p, void* out, const v
   a.v_scale = p->v_scale;
   bool ok = false;
   hipError_t e = pkv::launch_prefill(a, p->cache_dtype, p->head_dim, p->num_query_tokens, (hipStream_t)stream, &ok);
-  if (!ok) return pkv_fail(PKV_ERR_UNSUPPORTED, "prefill: no kernel variant");
+  if (!ok)
+    return pkv_fail(PKV_ERR_UNSUPPORTED,
+                    "prefill: no kernel for this shape (dtype / head_dim / block_size, more than 2^31 "
+                    "workgroups, or a physical block of all kv heads of 4 GiB or more)");
   return check_hip(e, "prefill launch");
 }
 

@@ -338,6 +338,12 @@ def test_prefill_validation():
     assert f(prefill_params(num_q_heads=6, num_kv_heads=4), *ok) == pkv.PKV_ERR_INVALID_ARG
     assert f(prefill_params(), None, 16, 16, 16, 16, 16, 16, None) == pkv.PKV_ERR_INVALID_ARG
     assert f(prefill_params(), 16, 16, 16, 16, 16, 16, 18, None) == pkv.PKV_ERR_INVALID_ARG
+    # a physical block of all kv heads of 4 GiB (262144 heads x 32 tokens x 128 x fp32): the
+    # kernel's block offsets are 32-bit stride x 32-bit id, so the launcher refuses it
+    big = dict(num_q_heads=1 << 18, num_kv_heads=1 << 18, block_size=32, q_dtype=0, cache_dtype=0,
+               out_dtype=0)
+    assert f(prefill_params(**big), *ok) == pkv.PKV_ERR_UNSUPPORTED
+    assert "4 GiB" in L.pkv_last_error().decode()
     assert f(prefill_params(num_query_tokens=0), None, None, None, None, None, None, None,
              None) == pkv.PKV_OK
     assert "prefill" in L.pkv_last_error().decode() or "decode" in L.pkv_last_error().decode()
