@@ -125,6 +125,15 @@ __device__ __forceinline__ float opaque_inf() {
   return r;
 }
 
+// max(a, b, c) in one instruction.  Written as asm: from fmaxf the compiler
+// first quiets possible signalling NaNs of the MFMA results, one more
+// instruction per operand.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Row max over the 16 lanes of a head (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float row_max(float v, float pinf) {
   uint32_t u = __float_as_uint(v);
@@ -165,7 +174,9 @@ __device__ __forceinline__ f32x4 pf_scores(const u32x4 (&kf)[Tile<KIND, D>::NK],
 }
 
 // Online-softmax state of one row tile: running max m (log2 units), the
-// bump threshold m + kLazyMax, the fp32 sum of the weights, and O^T.
+// bump threshold m + kLazyMax in raw-score units ((m + kLazyMax) / scale, so
+// a raw max is compared without scaling it), the fp32 sum of the weights,
+// and O^T.
 template <int KIND, int D>
 struct PfState {
   float m, thr, l;
@@ -200,6 +211,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   const float pinf = opaque_inf();
   const bool qneg = a.score_scale_log2 < 0.f;  // fold the sign into Q (exact)
   const float scl = qneg ? -a.score_scale_log2 : a.score_scale_log2;
+  const float inv_scl = scl > 0.f ? 1.f / scl : INFINITY;  // scale 0: no bump after the first
   const uint32_t qflip = !qneg ? 0u : (KIND == kF32 ? 0x80000000u : 0x80008000u);
   int L[NR];
   bool row_ok[NR];
@@ -369,25 +381,25 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
           if (MASK) v = u * 2 * kBS + 8 * q4 + 4 * h + i < L[k] ? v : -INFINITY;
           x[k][h * 4 + i] = v;
         }
-      const float m01 = __builtin_amdgcn_fmed3f(x[k][0], x[k][1], pinf);
-      const float m23 = __builtin_amdgcn_fmed3f(x[k][2], x[k][3], pinf);
-      const float m45 = __builtin_amdgcn_fmed3f(x[k][4], x[k][5], pinf);
-      const float m67 = __builtin_amdgcn_fmed3f(x[k][6], x[k][7], pinf);
-      mx[k] = fmaxf(fmaxf(m01, m23), fmaxf(m45, m67));  // this lane's max; the row's below
+      const float m3a = max3(x[k][0], x[k][1], x[k][2]);
+      const float m3b = max3(x[k][3], x[k][4], x[k][5]);
+      const float m2c = __builtin_amdgcn_fmed3f(x[k][6], x[k][7], pinf);
+      mx[k] = max3(m3a, m3b, m2c);  // this lane's max (raw); the row's below
       // always true on a row's first step; false for NaN
-      any = any || (live && mx[k] * scl > st[k].thr);
+      any = any || (live && mx[k] > st[k].thr);
     }
     return any;
   };
   // The row max across the 4 lanes of each row and which rows move their
   // running max: needed only when some lane's own max passed its row's
-  // threshold (scl > 0 keeps the scaling monotone, so the row's scaled max
-  // passes it exactly when one of its lanes' does).
+  // threshold (raw scores against a raw threshold: the row's max passes it
+  // exactly when one of its lanes' does).
   auto row_bumps = [&](float (&mx)[NR], bool (&bump)[NR], bool live) {
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
-      mx[k] = row_max(mx[k], pinf) * scl;
+      mx[k] = row_max(mx[k], pinf);
       bump[k] = live && mx[k] > st[k].thr;
+      mx[k] *= scl;
     }
   };
   // Move the running max before a step's weights are formed; O must already
@@ -398,7 +410,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       const float m_new = bump[k] ? mx[k] : st[k].m;
       const float alpha = __builtin_amdgcn_exp2f(st[k].m - m_new);
       st[k].m = m_new;
-      st[k].thr = m_new + kLazyMax;
+      st[k].thr = (m_new + kLazyMax) * inv_scl;
       st[k].l *= alpha;
 #pragma unroll
       for (int nt = 0; nt < T::NT; ++nt) st[k].acc.o[nt] *= alpha;
