@@ -736,6 +736,60 @@ def sim_bench(args):
                       "paged_over_static": round(ratio, 3), "runs": runs}), flush=True)
 
 
+def prefill_oracle_leg(spec, w, lens, chunks, qstart, q, out, lse, torch, threads):
+    """The oracle beside the prefill line: for the shortest and the longest
+    sequence, the first and the last (up to) 16 rows of its chunk (positions
+    L - C .. L - C + 15 and L - 16 .. L - 1) against the fp64 oracle.  Its
+    inputs are the generated pool bytes (prefill writes no pool byte) of the
+    sequence's blocks, gathered in table order with the tables of the
+    oracle's own allocator, and the generated Q rows.  Returns the parity of
+    those rows and the oracle's timing (its FLOP rate on them)."""
+    from oracle import oracle as O
+    import workloads
+    BS = spec.block_size
+    S = len(lens)
+    ob = O.BlockAllocator(w.num_blocks, BS, w.max_blocks, w.free_order)
+    workloads.allocate_context(ob, spec, lens)
+    _, tables_o, _ = ob.export(np.arange(S, dtype=np.int64))
+    host = OracleSample.host
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens))})
+    checks, secs, flops, rows_done = [], 0.0, 0.0, 0
+    for s in seqs:
+        L, C = int(lens[s]), int(chunks[s])
+        if C <= 0:
+            continue
+        n = -(-L // BS)
+        idx = torch.from_numpy(tables_o[s, :n].astype(np.int64)).to(w.k_cache.device)
+        kc = host(w.k_cache.index_select(0, idx), torch)
+        vc = host(w.v_cache.index_select(0, idx), torch)
+        table = np.arange(n, dtype=np.int32)[None, :]
+        m = min(16, C)
+        q0, q1 = int(qstart[s]), int(qstart[s + 1])
+        for ctx, lo in ((L - C + m, q0), (L, q1 - m)):
+            qr = np.ascontiguousarray(host(q[lo:lo + m], torch))
+            t0 = time.perf_counter()
+            ref, rlse = O.prefill_attention(qr, spec.q_dtype, kc, vc, spec.cache_dtype, table,
+                                            np.array([ctx], dtype=np.int32),
+                                            np.array([0, m], dtype=np.int32), spec.num_kv_heads, BS,
+                                            float(np.float32(w.scale)), w.k_scale, w.v_scale,
+                                            threads=threads)
+            secs += time.perf_counter() - t0
+            flops += 4.0 * spec.num_q_heads * spec.head_dim * sum(ctx - m + j + 1 for j in range(m))
+            rows_done += m
+            got = out[lo:lo + m].float().cpu().numpy()
+            checks.append(compare(spec, got, lse[lo:lo + m].cpu().numpy().astype(np.float64), ref,
+                                  rlse))
+    worst = max(checks, key=lambda r: (r["max_err"], r["lse_rel_err"]))
+    parity = dict(worst, lse_rel_err=max(r["lse_rel_err"] for r in checks),
+                  ok=all(r["ok"] for r in checks), seqs=len(seqs), rows=rows_done,
+                  how="first and last 16 rows of the chunks of the shortest and longest sequence")
+    cpu = {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle", "seconds": round(secs, 2), "cpu_model": cpu_model(),
+           "sample": f"{rows_done} query rows x {spec.num_q_heads} heads of {len(seqs)} sequences "
+                     f"(first and last 16 chunk rows each), fp64 attention on {threads} threads"}
+    return parity, cpu
+
+
 def prefill_bench(args):
     """Chunked-prefill attention: every sequence of the workload attends its
     last `chunk` tokens causally over its whole paged context (K/V already in
@@ -800,7 +854,16 @@ def prefill_bench(args):
                         "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                         "traffic": None, "flops_per_launch": flops,
                         "avg_launch_us": round(ms * 1e3, 2)}}
+    if not args.no_parity or not args.no_cpu_baseline:
+        parity, cpu = prefill_oracle_leg(spec, w, blens, chunks, qstart, q, out, lse, torch,
+                                         job_cores())
+        if not args.no_parity:
+            res["parity"] = parity
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
+    if not args.no_parity and not res["parity"]["ok"]:
+        sys.exit(1)
 
 
 if __name__ == "__main__":
