@@ -666,6 +666,14 @@ def test_prefill_full_sequences_and_overlong_chunks():
     assert np.all(got[1000:1002] == 0)
 
 
+
+@pytest.mark.parametrize("cache", [BF16, E4M3])
+def test_prefill_empty_chunks_and_contexts(cache):
+    """Sequences with no chunk (C = 0: no workgroup item), one with an empty
+    context as well, beside chunks that end inside a 32-token step and one
+    spanning whole steps; the other rows must be untouched by the empty ones."""
+    _prefill_case(cache, 128, 4, [0, 5, 300, 64, 33], [0, 0, 17, 64, 0], label="empty chunks")
+
 # ------------------------------------------------------------------- automatic prefix caching
 def test_prefix_cache_reuses_cached_kv_end_to_end():
     """K and V are a fixed function of (token id, position), as a model's
