@@ -368,7 +368,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   // The scale (> 0: a negative one was moved into Q) is applied inside the
   // exponent, p = 2^(s * scale - m).
   auto max_of = [&](const f32x4 (&sc)[NR][2], int u, auto masked, float (&x)[NR][8],
-                    float (&mx)[NR], bool (&bump)[NR], bool live) {
+                    float (&mx)[NR]) {
     constexpr bool MASK = decltype(masked)::value;
     bool any = false;
 #pragma unroll
@@ -386,7 +386,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       const float m2c = __builtin_amdgcn_fmed3f(x[k][6], x[k][7], pinf);
       mx[k] = max3(m3a, m3b, m2c);  // this lane's max (raw); the row's below
       // always true on a row's first step; false for NaN
-      any = any || (live && mx[k] > st[k].thr);
+      any = any || mx[k] > st[k].thr;
     }
     return any;
   };
@@ -394,11 +394,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   // running max: needed only when some lane's own max passed its row's
   // threshold (raw scores against a raw threshold: the row's max passes it
   // exactly when one of its lanes' does).
-  auto row_bumps = [&](float (&mx)[NR], bool (&bump)[NR], bool live) {
+  auto row_bumps = [&](float (&mx)[NR], bool (&bump)[NR]) {
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       mx[k] = row_max(mx[k], pinf);
-      bump[k] = live && mx[k] > st[k].thr;
+      bump[k] = mx[k] > st[k].thr;
       mx[k] *= scl;
     }
   };
@@ -503,9 +503,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   };
 
   if (n32 > 0) {
-    // Software pipeline over steps.  Stage u runs the MFMAs of step u + 1's
-    // scores and step u's P.V while the VALU forms step u's weights and step
-    // u + 1's row max, so matrix and vector work of one wave overlap.  Step j
+    // Software pipeline over steps.  Stage u issues the MFMAs of step u + 1's
+    // scores, then takes step u's row max (its scores finished a stage ago,
+    // so neither the max nor the branch on a bump waits for an MFMA), forms
+    // its weights on the VALU while those MFMAs run, and issues its P.V.  Step j
     // lives in LDS buffer j mod (PD + 2); its copies start right after the
     // barrier of stage j - PD - 1, into the buffer of step j - PD - 2, whose
     // last reads (stage j - PD - 2) precede that barrier.  Before the barrier
@@ -530,53 +531,44 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
     ids_of(PD + 1, id);
     vm_wait<PD * NCW>();
     __syncthreads();
-    {
-      f32x4 sc[NR][2];
-      scores_of(kv[0], sc);
-      float mx[NR];
-      bool bump[NR];
-      if (__builtin_amdgcn_ballot_w64(max_of(sc, 0, std::true_type(), x, mx, bump, true))) {
-        row_bumps(mx, bump, true);
-        rescale(mx, bump);
-      }
-    }
+    // Raw scores of the current step (sc[J % 2] in stage J) and of the next.
+    f32x4 sc[2][NR][2];
+    scores_of(kv[0], sc[0]);
     int u = 0;
 #define PKV_PF_STAGE(J, MASK)                                                            \
   {                                                                                      \
     constexpr int NB = C_::NBUF;                                                         \
     constexpr int BC = (J) % NB, BN = ((J) + 1) % NB, BI = ((J) + PD + 1) % NB;          \
-    const bool live = u + 1 < n32;                                                       \
     vm_wait<(PD - 1) * NCW>();                                                           \
     __syncthreads();                                                                     \
     copy_step(u + PD + 1, id, lds0 + BI * SB);                                           \
     ids_of(u + PD + 2, id);                                                              \
     VR vr[NVR];                                                                          \
     read_v(kv[BC], vr);                                                                  \
-    f32x4 scn[NR][2];                                                                    \
-    scores_of(kv[BN], scn);                                                              \
+    scores_of(kv[BN], sc[((J) + 1) % 2]);                                                \
+    float mx[NR];                                                                        \
+    bool bump[NR];                                                                       \
+    const bool any = max_of(sc[(J) % 2], u, std::integral_constant<bool, MASK>(), x, mx);  \
+    if (__builtin_amdgcn_ballot_w64(any)) {                                              \
+      row_bumps(mx, bump);                                                               \
+      rescale(mx, bump);                                                                 \
+    }                                                                                    \
     PB pw[NR][NPB];                                                                      \
     weights_of(x, std::integral_constant<bool, MASK>(), pw);                             \
     pv_of(vr, pw, u, MASK && (u + 1) * 2 * kBS > Lmax);                                  \
-    float mx[NR];                                                                        \
-    bool bump[NR];                                                                       \
-    const bool any = max_of(scn, u + 1, std::integral_constant<bool, MASK>(), x, mx, bump, live); \
-    if (__builtin_amdgcn_ballot_w64(any)) {                                              \
-      row_bumps(mx, bump, live);                                                         \
-      rescale(mx, bump);                                                                 \
-    }                                                                                    \
     ++u;                                                                                 \
   }
-    // Stage u may skip masking when steps u and u + 1 are seen in full.
+    // Stage u may skip masking when every row sees step u in full.
     constexpr int U = C_::NBUF;  // stages per unrolled round
-    static_assert(U == 4, "the stage loops below are written for 4 stages a round");
-    const int u_plain = u_full >= 1 ? (u_full - 1) / U * U : 0;
+    static_assert(U == 4 && U % 2 == 0, "the stage loops below are written for 4 stages a round");
+    const int u_plain = u_full / U * U;
     while (u < u_plain) {
       PKV_PF_STAGE(0, false)
       PKV_PF_STAGE(1, false)
       PKV_PF_STAGE(2, false)
       PKV_PF_STAGE(3, false)
     }
-    for (;;) {
+    while (u < n32) {
       PKV_PF_STAGE(0, true)
       if (u >= n32) break;
       PKV_PF_STAGE(1, true)
