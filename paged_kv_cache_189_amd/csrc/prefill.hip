@@ -19,7 +19,8 @@ namespace pkv {
 namespace {
 
 // ---------------------------------------------------------------- chunked prefill
-// One workgroup per (kv head g, sequence s, item of 4 * NR query tiles).  A
+// One workgroup of NWV waves per (kv head g, sequence s, item of NWV * NR
+// query tiles).  A
 // query tile holds tokens_per_tile = 16 / G query tokens of the chunk, row
 // r = token r / G, head r % G, so the G heads of a token share every K/V
 // fragment as in decode; wave w owns NR consecutive query tiles.  Row r's
@@ -27,9 +28,9 @@ namespace {
 // (causal); the workgroup walks the context up to its last row's position in
 // 32-token steps (two 16-token K/V tiles).  A step is copied from the pool
 // straight into LDS (global_load_lds, 16 bytes a lane, no registers in
-// between), a quarter of it by each wave, PD + 1 steps ahead of its P.V, into
-// PD + 2 buffers with one barrier per step; all four waves run their query
-// tiles against it, so a K/V byte is fetched once per 4 * NR query tiles.
+// between), an equal share by each wave, PD + 1 steps ahead of its P.V, into
+// PD + 2 buffers with one barrier per step; all waves run their query tiles
+// against it, so a K/V byte is fetched once per NWV * NR query tiles.
 // Rows past the chunk copy the wave's last row and are not written; rows with
 // p < 0 (chunk longer than the context) are written as zeros.
 //
@@ -40,15 +41,19 @@ namespace {
 // one dim: 16 contiguous bytes of a pool V row.  About 40 VALU instructions
 // of online softmax go with them.  Steps every row of the item sees in full
 // take a loop with no causal masking.
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 4  // waves per workgroup where a step has copies for them all
+#endif
 template <int KIND, int D>
 struct PrefillCfg {
   using T = Tile<KIND, D>;
   static constexpr int NR = KIND == kF32 ? 1 : 2;  // query tiles per wave
-  static constexpr int NWV = 4;                     // waves per workgroup
+  static constexpr int NC = T::BYTES / 1024;        // 1 KiB copies per 16-token tile
+  static constexpr int NWV = 4 * NC >= PKV_PREFILL_WAVES ? PKV_PREFILL_WAVES : 4;  // waves per workgroup
   static constexpr int PD = 2;                      // steps in flight past the one scored next
   static constexpr int NBUF = PD + 2;               // LDS step buffers
-  static constexpr int NC = T::BYTES / 1024;        // 1 KiB copies per 16-token tile
   static constexpr int NCW = 4 * NC / NWV;          // copies per wave per step
+  static_assert(NWV == 4 || NWV == 8, "waves per workgroup");
   static_assert(NCW >= 1 && (4 * NC) % NWV == 0, "step split");
   static_assert(PD * NCW <= 63, "vmcnt range");
 };
@@ -244,16 +249,15 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
 
   // The copies of a step: 4 * NC of 1 KiB, copy idx = (kind * 2 + tile) *
   // NC + c for K (kind 0) and V (kind 1) of tiles 2u, 2u + 1 and the tile's
-  // 1 KiB chunk c; wave w does idx = w + NWV * i.  With NC >= 4 copy i of
-  // every wave has kind and tile (i * NWV / NC) >> 1 and & 1; with NC < 4 a
-  // wave copies from the one tile (w / NC) & 1, of kind i (NC = 2) or w / 2
-  // (NC = 1).  A lane copies LDS unit c * 64 + lane of the tile (the step
+  // 1 KiB chunk c; wave w does idx = w + NWV * i.  With NC >= NWV copy i of
+  // every wave has kind and tile (i * NWV / NC) >> 1 and & 1; with NC < NWV
+  // (both powers of two) a wave copies from the one tile (w / NC) & 1, copy i
+  // of kind (NWV * i / NC + w / NC) >> 1.  A lane copies LDS unit c * 64 + lane of the tile (the step
   // layout above); a pool of 2^shift * 16-token blocks holds a tile's row
   // (K: 16 tokens x 16 bytes of one dim group; V: the 16 tokens of one dim)
   // at row * (row bytes << shift) from the tile's start.
-  constexpr bool BOTH = NC >= 4;  // each wave copies from both tiles of a step
+  constexpr bool BOTH = NC >= NWV;  // each wave copies from both tiles of a step
   const int wtile = BOTH ? 0 : (w / NC) & 1;
-  const bool wkind = NC == 1 && (w >> 1);  // NC = 1: this wave's one copy is V
   uint32_t csrc[NCW], cdst[NCW];
 #pragma unroll
   for (int i = 0; i < NCW; ++i) {
@@ -340,10 +344,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
         constexpr int NWV_ = C_::NWV;
         const int kh = i * NWV_ / NC;  // compile-time once unrolled
         src = (kh >> 1) ? vt[kh & 1] : kt[kh & 1];
-      } else if constexpr (NC == 2) {
-        src = i ? vt[0] : kt[0];
       } else {
-        src = wkind ? vt[0] : kt[0];
+        constexpr int NWV_ = C_::NWV;
+        src = ((NWV_ * i / NC + w / NC) >> 1) ? vt[0] : kt[0];
       }
       copy_to_lds(uniform_ptr(src), csrc[i], lds + cdst[i]);
     }
@@ -659,30 +662,41 @@ void prefill_kernel(PrefillArgs a) {
 
 }  // namespace
 
+namespace {
+// One workgroup per item of NWV * NR query tiles; items <= rows / tokens per
+// item + one partial item per sequence.
+template <int C_, int D_, int SH_>
+hipError_t launch_prefill_cfg(const PrefillArgs& a, int64_t num_rows, hipStream_t stream,
+                              bool* supported) {
+  using Cfg = PrefillCfg<C_, D_>;
+  const int per = a.tokens_per_tile * Cfg::NR * Cfg::NWV;
+  const int64_t items = (num_rows + per - 1) / per + a.num_seqs;
+  int64_t groups = (int64_t)a.num_kv_heads * items;
+  groups = (groups + 7) / 8 * 8;
+  if (groups > INT32_MAX) {
+    *supported = false;
+    return hipSuccess;
+  }
+  hipLaunchKernelGGL((prefill_kernel<C_, D_, SH_>), dim3((unsigned)groups), dim3(64 * Cfg::NWV), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_prefill(const PrefillArgs& a, int cache, int D, int64_t num_rows,
                           hipStream_t stream, bool* supported) {
   *supported = true;
   if (a.num_seqs == 0 || num_rows == 0) return hipSuccess;
-  // one workgroup per item of 4 * NR query tiles; items <= rows / tokens per
-  // item + one partial item per sequence
-  const int nr = cache == kF32 ? PrefillCfg<kF32, 128>::NR : PrefillCfg<kBF16, 128>::NR;
-  const int per = a.tokens_per_tile * nr * PrefillCfg<kBF16, 128>::NWV;
-  const int64_t items = (num_rows + per - 1) / per + a.num_seqs;
-  int64_t groups = (int64_t)a.num_kv_heads * items;
-  groups = (groups + 7) / 8 * 8;
   // the kernel computes block offsets as 32-bit stride x 32-bit block id
   const int64_t es = cache == kF32 ? 4 : (cache == kBF16 ? 2 : 1);
   const int64_t block_stride = ((int64_t)a.num_kv_heads * kBS * D * es) << a.block_shift;
-  if (groups > INT32_MAX || block_stride > (int64_t)UINT32_MAX) {
+  if (block_stride > (int64_t)UINT32_MAX) {
     *supported = false;
     return hipSuccess;
   }
-  const dim3 grid((unsigned)groups), block(64 * PrefillCfg<kBF16, 128>::NWV);
 #define PKV_PF(C_, D_, SH_)                                                           \
-  if (cache == C_ && D == D_ && a.block_shift == SH_) {                               \
-    hipLaunchKernelGGL((prefill_kernel<C_, D_, SH_>), grid, block, 0, stream, a);     \
-    return hipGetLastError();                                                         \
-  }
+  if (cache == C_ && D == D_ && a.block_shift == SH_)                                 \
+    return launch_prefill_cfg<C_, D_, SH_>(a, num_rows, stream, supported);
   PKV_PF(kF32, 64, 0) PKV_PF(kF32, 128, 0) PKV_PF(kBF16, 64, 0) PKV_PF(kBF16, 128, 0)
   PKV_PF(kFP8, 64, 0) PKV_PF(kFP8, 128, 0) PKV_PF(kF32, 64, 1) PKV_PF(kF32, 128, 1)
   PKV_PF(kBF16, 64, 1) PKV_PF(kBF16, 128, 1) PKV_PF(kFP8, 64, 1) PKV_PF(kFP8, 128, 1)
