@@ -180,11 +180,14 @@ __device__ __forceinline__ f32x4 pf_scores(const u32x4 (&kf)[Tile<KIND, D>::NK],
 
 // Online-softmax state of one row tile: running max m (log2 units), the
 // bump threshold m + kLazyMax in raw-score units ((m + kLazyMax) / scale, so
-// a raw max is compared without scaling it), the fp32 sum of the weights,
-// and O^T.
+// a raw max is compared without scaling it), the fp32 sum of the weights
+// (for the lse), the sum of the weights as P.V multiplies them (rounded to
+// bf16 for the MFMA; the output's normaliser, so that their rounding scales
+// numerator and denominator alike), and O^T.
 template <int KIND, int D>
 struct PfState {
   float m, thr, l;
+  f32x4 lr;  // (an MFMA of a ones operand with P: every element the row's sum)
   Acc<KIND, D> acc;
 };
 
@@ -304,6 +307,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
     st[k].m = -INFINITY;
     st[k].thr = -INFINITY;
     st[k].l = 0.f;
+    st[k].lr = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < T::NT; ++nt) st[k].acc.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -415,6 +419,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       st[k].m = m_new;
       st[k].thr = (m_new + kLazyMax) * inv_scl;
       st[k].l *= alpha;
+      st[k].lr *= alpha;
 #pragma unroll
       for (int nt = 0; nt < T::NT; ++nt) st[k].acc.o[nt] *= alpha;
     }
@@ -503,6 +508,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
           st[k].acc.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bitcast<bf16x8>(vv), pw[k][0], st[k].acc.o[nt], 0, 0, 0);
       }
     }
+    if constexpr (KIND != kF32) {  // the rounded weights' row sums, in the same unit
+      const bf16x8 one8 = bitcast<bf16x8>(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+      for (int k = 0; k < NR; ++k)
+        st[k].lr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(one8, pw[k][0], st[k].lr, 0, 0, 0);
+    }
   };
 
   if (n32 > 0) {
@@ -586,19 +597,24 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
     vm_wait<0>();
   }
 
+  // a row's sum over its four lanes (l, l ^ 16, l ^ 32, l ^ 48)
+  auto row_sum = [](float v) {
+    uint32_t u = __float_as_uint(v);
+    auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    u = __float_as_uint(v);
+    auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  };
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
-    uint32_t lu = __float_as_uint(st[k].l);
-    auto s16 = __builtin_amdgcn_permlane16_swap(lu, lu, false, false);
-    float lsum = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
-    lu = __float_as_uint(lsum);
-    auto s32 = __builtin_amdgcn_permlane32_swap(lu, lu, false, false);
-    lsum = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+    const float lsum = row_sum(st[k].l);
+    const float lnorm = KIND == kF32 ? lsum : st[k].lr[0];
     if (!row_ok[k]) continue;
     const int j = jbase + k * NQ + jl;
     const bool empty = Ls - C + j + 1 <= 0;
     const int64_t row = (int64_t)(q0 + j) * Hq + g * G + hh;
-    const float inv = !empty && lsum > 0.f ? a.v_scale / lsum : 0.f;
+    const float inv = !empty && lnorm > 0.f ? a.v_scale / lnorm : 0.f;
 #pragma unroll
     for (int nt = 0; nt < T::NT; ++nt) {
       const int d = nt * 16 + 4 * q4;

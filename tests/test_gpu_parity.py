@@ -646,9 +646,10 @@ def test_prefill_mixed_chunks(cache, D, group):
     _prefill_case(cache, D, group, PF_LENS, PF_CHUNKS, label=f"mixed")
 
 
-@pytest.mark.parametrize("cache", [BF16, E4M3])
-def test_prefill_block_size_32(cache):
-    _prefill_case(cache, 128, 4, PF_LENS, PF_CHUNKS, bs=32, label="bs32")
+@pytest.mark.parametrize("cache", [F32, BF16, E4M3])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_block_size_32(cache, D):
+    _prefill_case(cache, D, 4, PF_LENS, PF_CHUNKS, bs=32, label="bs32")
 
 
 @pytest.mark.parametrize("cache", [F32, BF16])
@@ -673,6 +674,18 @@ def test_prefill_empty_chunks_and_contexts(cache):
     context as well, beside chunks that end inside a 32-token step and one
     spanning whole steps; the other rows must be untouched by the empty ones."""
     _prefill_case(cache, 128, 4, [0, 5, 300, 64, 33], [0, 0, 17, 64, 0], label="empty chunks")
+
+@pytest.mark.parametrize("cache", [BF16, E4M3])
+def test_prefill_max_sequences(cache):
+    """The largest batch a prefill call takes, 1024 sequences: every
+    workgroup builds the item prefix sums over four 256-sequence rounds and
+    finds its sequence among all of them.  Short ragged contexts, chunks from
+    none to the whole context."""
+    rng = np.random.default_rng(31 + cache)
+    lens = rng.integers(0, 80, 1024)
+    chunks = np.minimum(lens, rng.integers(0, 48, 1024))
+    _prefill_case(cache, 128, 4, lens, chunks, label="1024 sequences")
+
 
 # ------------------------------------------------------------------- automatic prefix caching
 def test_prefix_cache_reuses_cached_kv_end_to_end():
