@@ -155,6 +155,20 @@ def test_more_than_1024_sequences(cache, part):
     full_parity(c, seqs, label=f"1100 seqs dtype={cache} part={part}")
 
 
+@pytest.mark.parametrize("cache", [BF16, E4M3])
+def test_short_contexts_every_row(cache):
+    """4096 sequences of 1 to 40 tokens, every output row against the oracle:
+    attention over a few tokens gives outputs as large as single V values,
+    where the bf16 roundings of P and of the output leave the least room
+    under the output bar."""
+    rng = np.random.default_rng(53 + cache)
+    lens = rng.integers(1, 41, 4096)
+    base = {BF16: 2, E4M3: 4}[cache]
+    spec = small_spec(270 + cache, base, len(lens), 32, 8, 128, lens, cache)
+    c = G.build(spec, partition_size=0)
+    full_parity(c, label=f"4096 short sequences dtype={cache}")
+
+
 @pytest.mark.parametrize("cache", [F32, BF16, E4M3])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
@@ -494,7 +508,7 @@ def test_cow_fork_diverge_and_multi_token_append(cache):
     if cache == F32:
         assert np.all(err <= 1e-5 * np.abs(ref).max(axis=2, keepdims=True))
     else:
-        assert err.max() <= G.TOL[cache], err.max()
+        assert np.all(err <= G.out_bound(ref, cache)), err.max()
     assert np.allclose(lse.cpu().numpy(), rlse, rtol=1e-4, atol=1e-4)
 
 
@@ -558,7 +572,7 @@ def test_block_size_32(cache, D, part):
     if cache == F32:
         assert np.all(err <= 1e-5 * np.abs(ref).max(axis=2, keepdims=True))
     else:
-        assert err.max() <= G.TOL[cache], err.max()
+        assert np.all(err <= G.out_bound(ref, cache)), err.max()
     assert np.allclose(lse.cpu().numpy(), rlse, rtol=1e-4, atol=1e-4)
 
 
@@ -626,7 +640,7 @@ def _prefill_case(cache, D, grp, lens, chunks, bs=16, Hkv=2, label="", scale=Non
         bound = 1e-5 * np.abs(ref).max(axis=2, keepdims=True)
         assert np.all(err <= np.maximum(bound, 1e-30)), f"{label}: fp32 err"
     else:
-        assert err.max() <= G_TOL[cache], f"{label}: max abs err {err.max()}"
+        assert np.all(err <= G.out_bound(ref, cache)), f"{label}: max abs err {err.max()}"
     gl = lse.cpu().numpy()
     fin = np.isfinite(rlse)
     assert np.array_equal(fin, np.isfinite(gl)), f"{label}: lse finiteness"
@@ -634,7 +648,6 @@ def _prefill_case(cache, D, grp, lens, chunks, bs=16, Hkv=2, label="", scale=Non
     return got, ref
 
 
-G_TOL = G.TOL
 PF_LENS = [1, 17, 100, 700, 2049, 3000]
 PF_CHUNKS = [1, 17, 37, 300, 1, 160]
 
@@ -749,8 +762,8 @@ def test_prefix_cache_reuses_cached_kv_end_to_end():
     torch.cuda.synchronize()
     ref, _ = O.decode_attention(q, BF16, k_all, v_all, BF16, tables, lens, Hkv, bs,
                                 float(np.float32(1 / math.sqrt(D))))
-    err = np.abs(out.float().cpu().numpy() - ref).max()
-    assert err <= G.TOL[BF16], err
+    err = np.abs(out.float().cpu().numpy() - ref)
+    assert np.all(err <= G.out_bound(ref, BF16)), err.max()
 
 
 # ------------------------------------------------------------------- decode append (cache + tables)
