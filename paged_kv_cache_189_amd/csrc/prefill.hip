@@ -255,8 +255,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   // 1 KiB chunk c; wave w does idx = w + NWV * i.  With NC >= NWV copy i of
   // every wave has kind and tile (i * NWV / NC) >> 1 and & 1; with NC < NWV
   // (both powers of two) a wave copies from the one tile (w / NC) & 1, copy i
-  // of kind (NWV * i / NC + w / NC) >> 1.  A lane copies LDS unit c * 64 + lane of the tile (the step
-  // layout above); a pool of 2^shift * 16-token blocks holds a tile's row
+  // of kind (NWV * i / NC + w / NC) >> 1.  A lane copies LDS unit c * 64 +
+  // lane of the tile (the step layout above); a pool of 2^shift * 16-token
+  // blocks holds a tile's row
   // (K: 16 tokens x 16 bytes of one dim group; V: the 16 tokens of one dim)
   // at row * (row bytes << shift) from the tile's start.
   constexpr bool BOTH = NC >= NWV;  // each wave copies from both tiles of a step
