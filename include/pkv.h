@@ -392,8 +392,7 @@ pkv_status pkv_decode_attention_noalloc(const pkv_decode_params* p, void* out, c
  * walks the table up to its last row's position.
  * Rounding: bf16 and fp8 caches multiply bf16-rounded weights into V and
  * normalise the output by the sum of those rounded weights (lse: by their
- * fp32 sum); with an fp8 cache at head_dim 128 the scores take q as two E4M3
- * terms under a power-of-two scale per row (about 8 significant bits). */
+ * fp32 sum). */
 typedef struct {
   int32_t num_seqs;
   int32_t num_q_heads;

@@ -178,94 +178,6 @@ __device__ __forceinline__ f32x4 pf_scores(const u32x4 (&kf)[Tile<KIND, D>::NK],
   return acc;
 }
 
-// fp8 K at D = 128: the scores run on the fp8 matrix path (one 16x16x128
-// E4M3 MFMA per term, K straight from LDS, no conversion), with Q carried as
-// two E4M3 terms under one power-of-two scale 2^e per row: hi = e4m3(q 2^-e),
-// lo = e4m3(q 2^-e - hi), e chosen so that the row's largest |q| 2^-e lies in
-// [128, 256).  hi + lo holds each q to about 2^-8 of itself (2^-16 of the
-// row's largest |q| at the least); the MFMA applies 2^e.  Operand bytes 0-15
-// of lane group g are dims (the MFMA's k) 16 g .. 16 g + 15, bytes 16-31 dims
-// 64 + 16 g .. + 15, for A and B alike -- the dims of the K reads below --
-// and lane 16 b + n gives the scale of column n's dims 32 b .. 32 b + 31, so
-// every lane of a row carries the row's one scale.
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-template <int KIND, int D>
-struct ScoresF8 {
-  static constexpr bool value = KIND == kFP8 && D == 128;
-};
-struct QF8 {
-  i32x8 hi, lo;
-  int scale;  // E8M0 code of 2^e
-};
-
-__device__ __forceinline__ QF8 q_to_f8(const u32x4 (&q)[4]) {
-  float v[32];
-#pragma unroll
-  for (int jq = 0; jq < 4; ++jq)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w = q[jq][e >> 1];
-      v[jq * 8 + e] = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
-    }
-  float mx = 0.f;
-  bool bad = false;  // an infinity or NaN in this lane's dims
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    mx = __builtin_fmaxf(mx, __builtin_fabsf(v[i]));
-    bad = bad || !(__builtin_fabsf(v[i]) <= 3.4028235e38f);
-  }
-  // the row's largest |q|, over its four lanes (l, l ^ 16, l ^ 32, l ^ 48)
-  uint32_t u = __float_as_uint(mx);
-  auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  mx = __builtin_fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-  u = __float_as_uint(mx);
-  auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  mx = __builtin_fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-  QF8 r;
-  int e = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 8 : 0;  // mx 2^-e in [128, 256)
-  e = e < -127 ? -127 : (e > 127 ? 127 : e);
-  const float sc = __builtin_ldexpf(1.f, -e);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a0 = v[4 * i] * sc, a1 = v[4 * i + 1] * sc, a2 = v[4 * i + 2] * sc, a3 = v[4 * i + 3] * sc;
-    int h = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
-    h = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, h, true);
-    const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(h, false);
-    const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(h, true);
-    int l = __builtin_amdgcn_cvt_pk_fp8_f32(a0 - h01[0], a1 - h01[1], 0, false);
-    l = __builtin_amdgcn_cvt_pk_fp8_f32(a2 - h23[0], a3 - h23[1], l, true);
-    r.hi[i] = bad ? 0x7F7F7F7F : h;  // NaN codes: NaN scores, as on the bf16 path
-    r.lo[i] = bad ? 0x7F7F7F7F : l;
-  }
-  r.scale = 127 + e;
-  return r;
-}
-
-// lo = K . Q_lo, then s = K . Q_hi + lo.  lo must stay in its registers until
-// s is read a stage later (StepScores::at keeps it alive): with the compiler's
-// wait-state count for this instruction, a vector-ALU write into the C
-// operand's registers eight cycles after the MFMA read them still corrupted
-// its result (the fp8 prefill parity tests failed that way).
-__device__ __forceinline__ void pf_scores_f8(const u32x4 (&kf)[2], const QF8& q, f32x4& s, f32x4& lo) {
-  const i32x8 k = bitcast<i32x8>(kf);
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  lo = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, q.lo, z, 0, 0, 0, 127, 0, q.scale);
-  s = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k, q.hi, lo, 0, 0, 0, 127, 0, q.scale);
-}
-
-// A step's raw scores for every row tile and 16-token tile: S^T[token 4 q4 +
-// i][row r] at s[k][h][i]; on the fp8 path t holds the lo term's accumulator,
-// the C operand of s's MFMA, kept in registers until s is read.
-template <int KIND, int D, int NR>
-struct StepScores {
-  f32x4 s[NR][2];
-  f32x4 t[ScoresF8<KIND, D>::value ? NR : 1][2];
-  __device__ __forceinline__ float at(int k, int h, int i) const {
-    if constexpr (ScoresF8<KIND, D>::value) asm volatile("" : : "v"(t[k][h]));
-    return s[k][h][i];
-  }
-};
-
 // Online-softmax state of one row tile: running max m (log2 units), the
 // bump threshold m + kLazyMax in raw-score units ((m + kLazyMax) / scale, so
 // a raw max is compared without scaling it), the fp32 sum of the weights
@@ -324,7 +236,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
               ((int64_t)(q0 + jj) * Hq + g * G + (r < NQ * G ? hh : 0)) * D * QES;
   }
   u32x4 q[NR][T::NQ];  // Q^T fragments, kept in registers for the whole item
-  QF8 qf[ScoresF8<KIND, D>::value ? NR : 1];  // ... or their E4M3 terms
   auto load_q = [&]() {
 #pragma unroll
     for (int k = 0; k < NR; ++k)
@@ -449,7 +360,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
   using PB = typename std::conditional<KIND == kF32, f32x4, bf16x8>::type;
   constexpr int NPB = KIND == kF32 ? 2 : 1;
   // S^T of a step for every row tile, from the step's K in LDS.
-  auto scores_of = [&](const PfStep<KIND, D>& t, StepScores<KIND, D, NR>& sc) {
+  auto scores_of = [&](const PfStep<KIND, D>& t, f32x4 (&sc)[NR][2]) {
     const char* kb = reinterpret_cast<const char*>(t.k);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -457,19 +368,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
 #pragma unroll
       for (int j = 0; j < T::NK; ++j) kf[j] = *reinterpret_cast<const u32x4*>(kb + koff[h] + j * 1024);
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        if constexpr (ScoresF8<KIND, D>::value)
-          pf_scores_f8(kf, qf[k], sc.s[k][h], sc.t[k][h]);
-        else
-          sc.s[k][h] = pf_scores<KIND, D>(kf, q[k]);
-      }
+      for (int k = 0; k < NR; ++k) sc[k][h] = pf_scores<KIND, D>(kf, q[k]);
     }
   };
   // Raw scores of step u (past each row's causal bound -> -inf when MASK),
   // each lane's max of them, and whether some row's running max must move.
   // The scale (> 0: a negative one was moved into Q) is applied inside the
   // exponent, p = 2^(s * scale - m).
-  auto max_of = [&](const StepScores<KIND, D, NR>& sc, int u, auto masked, float (&x)[NR][8],
+  auto max_of = [&](const f32x4 (&sc)[NR][2], int u, auto masked, float (&x)[NR][8],
                     float (&mx)[NR]) {
     constexpr bool MASK = decltype(masked)::value;
     bool any = false;
@@ -479,7 +385,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = sc.at(k, h, i);
+          float v = sc[k][h][i];
           if (MASK) v = u * 2 * kBS + 8 * q4 + 4 * h + i < L[k] ? v : -INFINITY;
           x[k][h * 4 + i] = v;
         }
@@ -638,14 +544,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, PfStep<KIND, 
       copy_step(j, id, lds0 + j * SB);
     }
     ids_of(PD + 1, id);
-    if constexpr (ScoresF8<KIND, D>::value) {
-#pragma unroll
-      for (int k = 0; k < NR; ++k) qf[k] = q_to_f8(q[k]);
-    }
     vm_wait<PD * NCW>();
     __syncthreads();
     // Raw scores of the current step (sc[J % 2] in stage J) and of the next.
-    StepScores<KIND, D, NR> sc[2];
+    f32x4 sc[2][NR][2];
     scores_of(kv[0], sc[0]);
     int u = 0;
 #define PKV_PF_STAGE(J, MASK)                                                            \

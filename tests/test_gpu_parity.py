@@ -611,13 +611,17 @@ def _paged_batch(gen, cache, D, Hkv, lens, bs=16, seed=0):
                 vsc=vsc, bs=bs)
 
 
-def _prefill_case(cache, D, grp, lens, chunks, bs=16, Hkv=2, label="", scale=None):
+def _prefill_case(cache, D, grp, lens, chunks, bs=16, Hkv=2, label="", scale=None, q_fn=None):
     gen = torch.Generator().manual_seed(1000 + 97 * cache + D + 7 * grp + bs)
     b = _paged_batch(gen, cache, D, Hkv, lens, bs, seed=grp + D)
     Hq = Hkv * grp
     qstart = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
     R = int(qstart[-1])
     q = _rand_storage(gen, (R, Hq, D), b["qd"])
+    if q_fn is not None:  # reshape the query values (fp32), then store them as the query dtype
+        qf = q.astype(np.float32) if b["qd"] == F32 else (q.astype(np.uint32) << 16).view(np.float32)
+        qf = torch.from_numpy(np.ascontiguousarray(q_fn(qf), dtype=np.float32))
+        q = qf.numpy() if b["qd"] == F32 else qf.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     dq = _to_device(q, b["qd"])
     out_t = torch.float32 if cache == F32 else torch.bfloat16
     d_tables = torch.from_numpy(b["tables"]).cuda()
@@ -644,7 +648,9 @@ def _prefill_case(cache, D, grp, lens, chunks, bs=16, Hkv=2, label="", scale=Non
     gl = lse.cpu().numpy()
     fin = np.isfinite(rlse)
     assert np.array_equal(fin, np.isfinite(gl)), f"{label}: lse finiteness"
-    assert np.allclose(gl[fin], rlse[fin], rtol=1e-4, atol=1e-4), f"{label}: lse"
+    lerr = np.abs(gl[fin] - rlse[fin]) / (1e-4 + 1e-4 * np.abs(rlse[fin])) if fin.any() else np.zeros(1)
+    G.log(f"[prefill {label}] max abs err {err.max():.3e}, lse err / bar {lerr.max():.3f}")
+    assert lerr.max() <= 1.0, f"{label}: lse"
     return got, ref
 
 
@@ -698,6 +704,31 @@ def test_prefill_max_sequences(cache):
     lens = rng.integers(0, 80, 1024)
     chunks = np.minimum(lens, rng.integers(0, 48, 1024))
     _prefill_case(cache, 128, 4, lens, chunks, label="1024 sequences")
+
+
+@pytest.mark.parametrize("cache", [BF16, E4M3])
+@pytest.mark.parametrize("gain", [4.0, 8.0])
+def test_prefill_sharp_softmax(cache, gain):
+    """Queries 4 and 8 times N(0, 1): scores with a spread of 6 to 12 in log2
+    units, so a few tokens carry most of each row's weight and a small score
+    error moves the output the most (with an fp8 cache the scores take q as
+    two E4M3 terms)."""
+    _prefill_case(cache, 128, 4, PF_LENS, PF_CHUNKS, label=f"sharp x{gain}",
+                  q_fn=lambda q: q * gain)
+
+
+@pytest.mark.parametrize("cache", [BF16, E4M3])
+def test_prefill_query_rows_of_any_size(cache):
+    """Query rows scaled by 2^-24 .. 2^6 and one dim per row 64 times the
+    others: the fp8 score path scales each row by its own power of two."""
+    def q_fn(q):
+        rng = np.random.default_rng(17)
+        R, Hq, D = q.shape
+        q = q * np.exp2(rng.integers(-24, 7, size=(R, Hq, 1))).astype(np.float32) / 64
+        d = rng.integers(0, D, size=(R, Hq, 1))
+        np.put_along_axis(q, d, np.take_along_axis(q, d, 2) * 64, 2)
+        return q
+    _prefill_case(cache, 128, 4, PF_LENS, PF_CHUNKS, label="row sizes", q_fn=q_fn)
 
 
 # ------------------------------------------------------------------- automatic prefix caching
