@@ -81,6 +81,19 @@ def test_ragged_lengths(cache, part):
     full_parity(c, label=f"ragged dtype={cache} part={part}")
 
 
+@pytest.mark.parametrize("cache", [BF16, E4M3])
+@pytest.mark.parametrize("part", [0, 64])
+def test_decode_sharp_softmax(cache, part):
+    """Queries 8 times N(0, 1) (exact in bf16): scores spread over ~12 in log2
+    units, so a few tokens carry each row and the lazy running max moves more
+    often; output and lse against the oracle."""
+    base = {BF16: 2, E4M3: 4}[cache]
+    spec = small_spec(205 + cache, base, len(RAGGED), 32, 8, 128, RAGGED, cache)
+    c = G.build(spec, partition_size=part)
+    c.w.q.mul_(8.0)
+    full_parity(c, label=f"sharp dtype={cache} part={part}")
+
+
 @pytest.mark.parametrize("cache", [F32, BF16, E4M3])
 def test_many_ranges_per_sequence(cache):
     """Enough blocks that every pass-1 range is busy: long sequences span many
