@@ -265,7 +265,7 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype,
  * 1 <= Hq / Hkv <= 16; partition_size = 0 (no partition cuts) or a
  * positive multiple of block_size.  context_lens must lie in [0, max_context_len] and
  * max_context_len <= max_blocks_per_seq * block_size; table entries of the
- * first ceil(L_s / 16) columns must be < num_blocks.  Other entries and slots
+ * first ceil(L_s / block_size) columns must be < num_blocks.  Other entries and slots
  * past L_s are never read (they may hold anything, NaN included).  Out-of-
  * range lengths are clamped and out-of-range block ids are clamped into the
  * pool, so a bad input never reads outside the buffers; its output is then
