@@ -89,6 +89,13 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
     if constexpr (SRC == kF32) return __uint_as_float(bits32(r, x));
     else return __uint_as_float((uint32_t)bits16(r, x) << 16);
   };
+  constexpr bool kStream = CACHE != kFP8;  // store policy (below)
+  auto put = [](auto* p, auto v) {
+    if constexpr (kStream)
+      __builtin_nontemporal_store(v, p);
+    else
+      *p = v;
+  };
   for (int e = threadIdx.x; e < items; e += blockDim.x) {
     Raw kr = k0, vr = v0;
     if (e != (int)threadIdx.x) {
@@ -99,12 +106,16 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
     const int64_t tile = (blk * a.num_kv_heads + h);
     const int64_t kdst = ((tile * CH + c) * B + off) * X;  // element index
     const int64_t vdst = (tile * D + c * X) * B + off;     // element index, stride B
-    // A word of every destination line is read before the stores, so the
-    // L2 holds those lines whole when the stores land and writes them back
-    // whole.  The decode attention that next reads them measured 0.4-1.5%
-    // faster so (70B-shaped fp8 and shared-prefix bf16 batches); partial
-    // lines written back are the likely cost (the memory merges them).
-    {
+    // Cache policy of the stores, measured per cache dtype on the decode
+    // step (this write, then the attention over the new tokens).  bf16 and
+    // fp32 stores stream past the L2 (non-temporal), so the attention meets
+    // no dirty lines of theirs (steps 2.4% and 1% faster on the 70B-shaped
+    // shared-prefix and the Llama-3-8B-shaped bf16 batches).  Streamed fp8
+    // stores (single bytes of V) slowed this kernel more than they saved the
+    // attention, so the L2 takes them; a word of every destination line is
+    // read first so that it holds those lines whole (0.4-0.5% faster steps
+    // on the 70B-shaped fp8 batch than with either plain or streamed stores).
+    if constexpr (!kStream) {
       uint32_t old = *reinterpret_cast<const uint32_t*>(static_cast<const char*>(a.k_cache) + kdst * ES);
 #pragma unroll
       for (int x = 0; x < X; ++x) old += static_cast<const uint8_t*>(a.v_cache)[(vdst + x * B) * ES];
@@ -116,15 +127,15 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
       if constexpr (ES == 4) {
         uint32_t* kc = static_cast<uint32_t*>(a.k_cache);
         uint32_t* vc = static_cast<uint32_t*>(a.v_cache);
-        *reinterpret_cast<u32x4*>(kc + kdst) = kr.q[0];
+        put(reinterpret_cast<u32x4*>(kc + kdst), kr.q[0]);
 #pragma unroll
-        for (int x = 0; x < X; ++x) vc[vdst + x * B] = bits32(vr, x);
+        for (int x = 0; x < X; ++x) put(vc + vdst + x * B, bits32(vr, x));
       } else {
         uint16_t* kc = static_cast<uint16_t*>(a.k_cache);
         uint16_t* vc = static_cast<uint16_t*>(a.v_cache);
-        *reinterpret_cast<u32x4*>(kc + kdst) = kr.q[0];
+        put(reinterpret_cast<u32x4*>(kc + kdst), kr.q[0]);
 #pragma unroll
-        for (int x = 0; x < X; ++x) vc[vdst + x * B] = bits16(vr, x);
+        for (int x = 0; x < X; ++x) put(vc + vdst + x * B, bits16(vr, x));
       }
     } else if constexpr (CACHE == kBF16) {  // f32 -> bf16
       uint16_t* kc = static_cast<uint16_t*>(a.k_cache);
@@ -132,18 +143,18 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
       uint16_t kv[X];
 #pragma unroll
       for (int x = 0; x < X; ++x) kv[x] = f32_to_bf16_rne(val(kr, x));
-      *reinterpret_cast<u32x4*>(kc + kdst) = bitcast<u32x4>(kv);
+      put(reinterpret_cast<u32x4*>(kc + kdst), bitcast<u32x4>(kv));
 #pragma unroll
-      for (int x = 0; x < X; ++x) vc[vdst + x * B] = f32_to_bf16_rne(val(vr, x));
+      for (int x = 0; x < X; ++x) put(vc + vdst + x * B, f32_to_bf16_rne(val(vr, x)));
     } else {  // -> fp8 E4M3 of fp32(x / scale)
       uint8_t* kc = static_cast<uint8_t*>(a.k_cache);
       uint8_t* vc = static_cast<uint8_t*>(a.v_cache);
       uint8_t kv[X];
 #pragma unroll
       for (int x = 0; x < X; ++x) kv[x] = f32_to_e4m3_sat(val(kr, x) / a.k_scale);
-      *reinterpret_cast<u32x4*>(kc + kdst) = bitcast<u32x4>(kv);
+      put(reinterpret_cast<u32x4*>(kc + kdst), bitcast<u32x4>(kv));
 #pragma unroll
-      for (int x = 0; x < X; ++x) vc[vdst + x * B] = f32_to_e4m3_sat(val(vr, x) / a.v_scale);
+      for (int x = 0; x < X; ++x) put(vc + vdst + x * B, f32_to_e4m3_sat(val(vr, x) / a.v_scale));
     }
   }
 }
