@@ -109,8 +109,8 @@ __global__ __launch_bounds__(128) void cache_write_kernel(CacheWriteArgs a) {
     // Cache policy of the stores, measured per cache dtype on the decode
     // step (this write, then the attention over the new tokens).  bf16 and
     // fp32 stores stream past the L2 (non-temporal), so the attention meets
-    // no dirty lines of theirs (steps 2.4% and 1% faster on the 70B-shaped
-    // shared-prefix and the Llama-3-8B-shaped bf16 batches).  Streamed fp8
+    // no dirty lines of theirs (steps 2.4-2.8% faster on the 70B-shaped
+    // shared-prefix bf16 batch, within 1% on the others).  Streamed fp8
     // stores (single bytes of V) slowed this kernel more than they saved the
     // attention, so the L2 takes them; a word of every destination line is
     // read first so that it holds those lines whole (0.4-0.5% faster steps
